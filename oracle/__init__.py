@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for the fused-attention path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import anything under ``oracle/``.  The library's product path
+(the C ABI in ``include/fa.h`` and its Python binding) never calls it, and
+the two share no code.
+"""
+from .attention import attention, decode, visible, visible_matrix  # noqa: F401

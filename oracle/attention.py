@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for fused attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the package smoke check and the benchmark's CPU
+baseline may import this module.  The library's product path never routes
+through it; the two share no code.
+
+What it computes
+----------------
+The plain three-step definition of scaled dot-product attention, written out
+in float64 with NumPy:
+
+1. scores      S = scale * Q K^T
+   (ops-transformer practice page, jsqmd.com, section 二 "SelfAttention
+   baseline and its bottleneck": Attention(Q,K,V) = softmax(QK^T/sqrt(d)) V;
+   the naive_attention listing of section 二 "fused computation idea" and the
+   BertSelfAttention forward of the agent.csdn.net BERT page, chapter 一,
+   take the same three steps: matmul, softmax, matmul.)
+2. mask        masked scores are set to -inf, so they vanish after softmax
+   (jsqmd.com page, section 二 "causal mask and decode": the upper triangle
+   is set to negative infinity; agent.csdn.net BERT page, chapter 四:
+   padding positions are masked to negative infinity and so change nothing).
+3. softmax     row-wise with the row maximum subtracted before exp
+   (hwcomputing.csdn.net page, section 2.2: softmax(x_i) =
+   exp(x_i - max x) / sum_j exp(x_j - max x)).
+4. output      O = P V and the natural-log log-sum-exp per row,
+   LSE_i = m_i + ln(sum_j exp(S_ij - m_i)).
+
+Readings taken where the pages are silent (each also listed in the design
+notes):
+
+* scale is one multiplier on QK^T (``softmax_scale``), converted to float64
+  from its float32 value;
+* valid lengths: query rows ``i >= Lq`` and keys ``j >= Lk`` are not visible
+  (the ``actual_seq_q`` / ``actual_seq_kv`` arguments of the BERT page,
+  chapter 三 and its closing section);
+* causal alignment is bottom-right: query row ``i`` sits at key position
+  ``pos_i = i + Lk - Lq`` and sees keys ``j <= pos_i``;
+* sliding window ``W >= 1`` keeps keys ``j > pos_i - W`` (W keys including
+  the diagonal); ``W = -1`` means no window;
+* grouped-query attention maps query head ``h`` to key/value head
+  ``h // (Hq // Hkv)`` (contiguous groups); MQA is ``Hkv = 1``;
+* a row with no visible key has O = 0 and LSE = -inf (instead of 0/0);
+* decode (the BERT page's closing section: the new token attends to all
+  cached keys, the cache is not recomputed) is the same computation with a
+  single query at position ``L_b - 1`` over cache rows ``0 .. L_b - 1``.
+
+Every function here is pinned in ``tests/test_oracle.py`` against closed
+forms, brute force on tiny integer inputs, library routines and invariants.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def visible(i: int, j: int, Lq: int, Lk: int, causal: bool, window_left: int) -> bool:
+    """Visibility of key ``j`` to query row ``i`` (scalar form of the mask)."""
+    if i < 0 or j < 0 or i >= Lq or j >= Lk:
+        return False
+    pos = i + (Lk - Lq)
+    if causal and j > pos:
+        return False
+    if window_left > 0 and j <= pos - window_left:
+        return False
+    return True
+
+
+def visible_matrix(rows: np.ndarray, Nk: int, Lq: int, Lk: int, causal: bool,
+                   window_left: int) -> np.ndarray:
+    """Boolean mask ``[len(rows), Nk]``: True where key j is visible to row i."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(Nk, dtype=np.int64)[None, :]
+    pos = i + (Lk - Lq)
+    vis = (i < Lq) & (j < Lk)
+    if causal:
+        vis &= j <= pos
+    if window_left > 0:
+        vis &= j > pos - window_left
+    return vis
+
+
+def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                 vis: np.ndarray):
+    """Three-step attention for one (batch, head): q_rows [r, d], k/v [Nk, d]."""
+    s = scale * (q_rows @ k.T)                       # step 1
+    s = np.where(vis, s, NEG_INF)                    # step 2
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    p = np.exp(s - m_safe[:, None])                  # step 3 (exp(-inf) = 0)
+    l = p.sum(axis=1)
+    # step 4 sums over visible keys only: keys no row can see are left out of
+    # the product, so that their stored values (e.g. NaN padding) never enter
+    # it as 0 * NaN.
+    cols = vis.any(axis=0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = (p[:, cols] @ v[cols]) / l[:, None]
+        lse = m_safe + np.log(l)
+    o[empty] = 0.0
+    lse[empty] = NEG_INF
+    return o, lse
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
+              causal: bool = False, window_left: int = -1,
+              seqlens_q: Optional[Sequence[int]] = None,
+              seqlens_k: Optional[Sequence[int]] = None,
+              rows: Optional[Sequence[int]] = None,
+              heads: Optional[Sequence[int]] = None):
+    """Reference attention forward.
+
+    q: [B, Nq, Hq, d], k and v: [B, Nk, Hkv, d] (any real dtype; used as
+    float64).  Returns ``(O, LSE)`` with O: [B, R, Hq', d] float64 and LSE:
+    [B, Hq', R] float64, where R = Nq (or ``len(rows)``) and Hq' = Hq (or
+    ``len(heads)``).  ``rows`` / ``heads`` restrict the computation to a
+    subset of query rows / heads; each output row depends only on its own
+    query and visible keys, so a subset is exact.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k, v")
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    scale = float(np.float32(scale))
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    heads = np.arange(Hq) if heads is None else np.asarray(heads, dtype=np.int64)
+    o = np.zeros((B, len(rows), len(heads), d), dtype=np.float64)
+    lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
+    for b in range(B):
+        Lq = Nq if seqlens_q is None else int(seqlens_q[b])
+        Lk = Nk if seqlens_k is None else int(seqlens_k[b])
+        vis = visible_matrix(rows, Nk, Lq, Lk, causal, window_left)
+        for hi, h in enumerate(heads):
+            kvh = h // group
+            ob, lb = _attend_rows(q[b, rows, h, :], k[b, :, kvh, :], v[b, :, kvh, :],
+                                  scale, vis)
+            o[b, :, hi, :] = ob
+            lse[b, hi, :] = lb
+    return o, lse
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+           seqlens_k: Sequence[int], *, scale: float, window_left: int = -1,
+           batches: Optional[Sequence[int]] = None):
+    """Reference single-token decode over a contiguous BSHD cache.
+
+    q: [B, Hq, d]; caches: [B, capacity, Hkv, d]; seqlens_k: [B] (clamped to
+    [0, capacity]).  The query of sequence b sits at position L_b - 1 and
+    sees cache rows 0 .. L_b - 1 (restricted by the window if W >= 1).
+    Returns O: [B', Hq, d] and LSE: [B', Hq] in float64.  Only the valid
+    prefix of each cache is read, so poisoned rows beyond it never matter.
+    """
+    B, Hq, d = q.shape
+    cap = k_cache.shape[1]
+    batches = range(B) if batches is None else batches
+    batches = list(batches)
+    o = np.zeros((len(batches), Hq, d), dtype=np.float64)
+    lse = np.zeros((len(batches), Hq), dtype=np.float64)
+    for bi, b in enumerate(batches):
+        L = int(min(max(int(seqlens_k[b]), 0), cap))
+        ob, lb = attention(q[b][None, None], k_cache[b, :L][None], v_cache[b, :L][None],
+                           scale=scale, causal=True, window_left=window_left,
+                           seqlens_q=[1], seqlens_k=[L])
+        o[bi] = ob[0, 0]
+        lse[bi] = lb[0, :, 0]
+    return o, lse

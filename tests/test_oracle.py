@@ -1,0 +1,423 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: hand-written
+visibility tables, closed forms, a scalar brute-force loop, library
+routines (torch SDPA, scipy logsumexp) and invariants the mathematics fixes.
+A plausible slip in the oracle (a dropped mask term, a wrong sign of the
+causal offset, a transposed operand, a missing max subtraction, a wrong GQA
+map, a log base) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f64(p):
+    return (workloads.to_f64(p.q, p.dtype), workloads.to_f64(p.k, p.dtype),
+            workloads.to_f64(p.v, p.dtype))
+
+
+# ---------------------------------------------------------------------------
+# P11: brute force on 4x4 with literal visibility tables
+# ---------------------------------------------------------------------------
+# (causal, window_left, seqlen_q, seqlen_k) -> visible[i][j], written by hand
+LITERAL_4x4 = {
+    (False, -1, 4, 4): [[1, 1, 1, 1]] * 4,
+    (True, -1, 4, 4): [[1, 0, 0, 0], [1, 1, 0, 0], [1, 1, 1, 0], [1, 1, 1, 1]],
+    (True, 1, 4, 4): [[1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0], [0, 0, 0, 1]],
+    (True, 2, 4, 4): [[1, 0, 0, 0], [1, 1, 0, 0], [0, 1, 1, 0], [0, 0, 1, 1]],
+    (True, 3, 4, 4): [[1, 0, 0, 0], [1, 1, 0, 0], [1, 1, 1, 0], [0, 1, 1, 1]],
+    (True, 4, 4, 4): [[1, 0, 0, 0], [1, 1, 0, 0], [1, 1, 1, 0], [1, 1, 1, 1]],
+    (False, 2, 4, 4): [[1, 1, 1, 1], [1, 1, 1, 1], [0, 1, 1, 1], [0, 0, 1, 1]],
+    (False, -1, 4, 2): [[1, 1, 0, 0]] * 4,
+    (False, -1, 4, 0): [[0, 0, 0, 0]] * 4,
+    (False, -1, 2, 4): [[1, 1, 1, 1], [1, 1, 1, 1], [0, 0, 0, 0], [0, 0, 0, 0]],
+    (False, -1, 0, 4): [[0, 0, 0, 0]] * 4,
+    # bottom-right causal, fewer keys than queries: rows 0 and 1 see nothing
+    (True, -1, 4, 2): [[0, 0, 0, 0], [0, 0, 0, 0], [1, 0, 0, 0], [1, 1, 0, 0]],
+    # bottom-right causal, fewer queries than keys
+    (True, -1, 2, 4): [[1, 1, 1, 0], [1, 1, 1, 1], [0, 0, 0, 0], [0, 0, 0, 0]],
+    (True, -1, 2, 2): [[1, 0, 0, 0], [1, 1, 0, 0], [0, 0, 0, 0], [0, 0, 0, 0]],
+    (True, 2, 3, 4): [[1, 1, 0, 0], [0, 1, 1, 0], [0, 0, 1, 1], [0, 0, 0, 0]],
+    (True, 1, 4, 3): [[0, 0, 0, 0], [1, 0, 0, 0], [0, 1, 0, 0], [0, 0, 1, 0]],
+}
+
+
+def _scalar_attention(q, k, v, scale, vis):
+    """Scalar loop: softmax weights with math.exp, no NumPy reductions."""
+    n_q, d = len(q), len(q[0])
+    out, lse = [], []
+    for i in range(n_q):
+        scores = []
+        for j in range(len(k)):
+            if vis[i][j]:
+                s = 0.0
+                for t in range(d):
+                    s += q[i][t] * k[j][t]
+                scores.append((j, scale * s))
+        if not scores:
+            out.append([0.0] * d)
+            lse.append(-math.inf)
+            continue
+        mx = max(s for _, s in scores)
+        w = [(j, math.exp(s - mx)) for j, s in scores]
+        tot = sum(x for _, x in w)
+        out.append([sum(x * v[j][t] for j, x in w) / tot for t in range(d)])
+        lse.append(mx + math.log(tot))
+    return out, lse
+
+
+@pytest.mark.parametrize("key", sorted(LITERAL_4x4, key=str))
+def test_bruteforce_4x4_literal_tables(key):
+    causal, window, Lq, Lk = key
+    table = np.array(LITERAL_4x4[key], dtype=bool)
+    got = oracle.visible_matrix(np.arange(4), 4, Lq, Lk, causal, window)
+    np.testing.assert_array_equal(got, table)
+    for i in range(4):
+        for j in range(4):
+            assert oracle.visible(i, j, Lq, Lk, causal, window) == table[i, j]
+
+    rng = np.random.default_rng(11)
+    d = 3
+    q = rng.integers(-2, 3, size=(4, d)).astype(np.float64)
+    k = rng.integers(-2, 3, size=(4, d)).astype(np.float64)
+    v = rng.integers(-3, 4, size=(4, d)).astype(np.float64)
+    scale = 0.5
+    o, lse = oracle.attention(q[None, :, None], k[None, :, None], v[None, :, None],
+                              scale=scale, causal=causal, window_left=window,
+                              seqlens_q=[Lq], seqlens_k=[Lk])
+    eo, el = _scalar_attention(q.tolist(), k.tolist(), v.tolist(), scale, table.tolist())
+    np.testing.assert_allclose(o[0, :, 0], np.array(eo), rtol=0, atol=1e-13)
+    for a, b in zip(lse[0, 0], el):
+        if math.isinf(b):
+            assert a == -math.inf
+        else:
+            assert abs(a - b) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# P1: Q = 0 -> O is the mean of the visible V rows and LSE = ln(#visible)
+# ---------------------------------------------------------------------------
+def _closed_form_range(i, Lq, Lk, causal, W):
+    """[lo, hi) of visible keys for row i, written from the definitions."""
+    if i >= Lq:
+        return 0, 0
+    pos = i + Lk - Lq
+    hi = min(Lk, pos + 1) if causal else Lk
+    lo = max(0, pos - W + 1) if W > 0 else 0
+    return lo, max(lo, hi)
+
+
+@pytest.mark.parametrize("causal,W,Lq,Lk,Hq,Hkv", [
+    (False, -1, 37, 37, 2, 2), (True, -1, 37, 37, 4, 2), (True, 5, 37, 37, 4, 1),
+    (False, 7, 37, 37, 2, 1), (False, -1, 37, 20, 3, 3), (True, -1, 20, 37, 2, 1),
+    (True, 9, 37, 29, 6, 2), (True, -1, 37, 0, 2, 2),
+])
+def test_zero_query_closed_form(causal, W, Lq, Lk, Hq, Hkv):
+    Nq, Nk, d = 37, 37, 8
+    rng = np.random.default_rng(3)
+    q = np.zeros((1, Nq, Hq, d))
+    k = rng.standard_normal((1, Nk, Hkv, d))
+    # distinct V per kv head so that a wrong GQA map is visible
+    v = rng.standard_normal((1, Nk, Hkv, d)) + 10.0 * np.arange(Hkv)[None, None, :, None]
+    o, lse = oracle.attention(q, k, v, scale=0.125, causal=causal, window_left=W,
+                              seqlens_q=[Lq], seqlens_k=[Lk])
+    G = Hq // Hkv
+    for i in range(Nq):
+        lo, hi = _closed_form_range(i, Lq, Lk, causal, W)
+        for h in range(Hq):
+            if hi == lo:
+                assert np.all(o[0, i, h] == 0.0)
+                assert lse[0, h, i] == -np.inf
+            else:
+                np.testing.assert_allclose(o[0, i, h], v[0, lo:hi, h // G].mean(axis=0),
+                                           rtol=0, atol=1e-12)
+                assert abs(lse[0, h, i] - math.log(hi - lo)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P2 / P3 / P4: identical V rows, identical K rows, single visible key
+# ---------------------------------------------------------------------------
+def test_identical_v_rows_return_that_row():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 33, 4, 16))
+    k = rng.standard_normal((2, 33, 2, 16))
+    row = rng.standard_normal(16)
+    v = np.broadcast_to(row, (2, 33, 2, 16)).copy()
+    o, _ = oracle.attention(q, k, v, scale=0.25, causal=True, window_left=6,
+                            seqlens_k=[33, 21])
+    # every non-empty row returns the common V row
+    _, lse = oracle.attention(q, k, v, scale=0.25, causal=True, window_left=6,
+                              seqlens_k=[33, 21])
+    nonempty = np.isfinite(lse).transpose(0, 2, 1)       # [B, N, H]
+    np.testing.assert_allclose(o[nonempty], np.broadcast_to(row, o[nonempty].shape),
+                               rtol=0, atol=1e-12)
+
+
+def test_identical_k_rows_give_visible_mean_any_q():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 40, 2, 8)) * 3
+    krow = rng.standard_normal(8)
+    k = np.broadcast_to(krow, (1, 40, 2, 8)).copy()
+    v = rng.standard_normal((1, 40, 2, 8))
+    scale = 0.3
+    o, lse = oracle.attention(q, k, v, scale=scale, causal=True, window_left=11)
+    for i in range(40):
+        lo, hi = _closed_form_range(i, 40, 40, True, 11)
+        for h in range(2):
+            np.testing.assert_allclose(o[0, i, h], v[0, lo:hi, h].mean(axis=0), atol=1e-12)
+            expect = float(np.float32(scale)) * float(q[0, i, h] @ krow) + math.log(hi - lo)
+            assert abs(lse[0, h, i] - expect) < 1e-11
+
+
+def test_causal_row0_is_v0_exactly():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 16, 1, 32))
+    k = rng.standard_normal((1, 16, 1, 32))
+    v = rng.standard_normal((1, 16, 1, 32))
+    o, lse = oracle.attention(q, k, v, scale=0.2, causal=True)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
+    assert abs(lse[0, 0, 0] - float(np.float32(0.2)) * float(q[0, 0, 0] @ k[0, 0, 0])) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# P6 / P7 / P8: shift, permutation and padding invariances
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shift", [0.5, 1000.0])
+def test_key_shift_invariance(shift):
+    """K -> K + 1 u^T adds scale*q_i.u to every score of row i."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 30, 2, 8))
+    k = rng.standard_normal((1, 30, 2, 8))
+    v = rng.standard_normal((1, 30, 2, 8))
+    u = np.full(8, shift)
+    scale = 0.5
+    o1, l1 = oracle.attention(q, k, v, scale=scale, causal=True, window_left=9)
+    o2, l2 = oracle.attention(q, k + u, v, scale=scale, causal=True, window_left=9)
+    assert np.all(np.isfinite(o2))
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-9)
+    delta = scale * np.einsum("bnhd,d->bhn", q, u)
+    np.testing.assert_allclose(l2, l1 + delta, rtol=1e-12, atol=1e-9)
+
+
+def test_joint_key_permutation_invariance():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((2, 19, 4, 8))
+    k = rng.standard_normal((2, 23, 2, 8))
+    v = rng.standard_normal((2, 23, 2, 8))
+    perm = rng.permutation(23)
+    o1, l1 = oracle.attention(q, k, v, scale=0.4)
+    o2, l2 = oracle.attention(q, k[:, perm], v[:, perm], scale=0.4)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+
+
+def test_padding_equivalence_with_poison():
+    p = workloads.make_prefill(21, 3, 50, 50, 4, 2, 16, "bf16", causal=True,
+                               seqlens_k_range=(1, 50), seqlens_q_equal_k=True,
+                               poison_padding=True)
+    q, k, v = _f64(p)
+    o, lse = oracle.attention(q, k, v, scale=p.scale, causal=True,
+                              seqlens_q=p.seqlens_q, seqlens_k=p.seqlens_k)
+    for b in range(3):
+        L = int(p.seqlens_k[b])
+        o_ref, l_ref = oracle.attention(q[b:b + 1, :L], k[b:b + 1, :L], v[b:b + 1, :L],
+                                        scale=p.scale, causal=True)
+        np.testing.assert_allclose(o[b, :L], o_ref[0], atol=1e-12)
+        np.testing.assert_allclose(lse[b, :, :L], l_ref[0], atol=1e-12)
+        assert np.all(o[b, L:] == 0.0) and np.all(lse[b, :, L:] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# P9: library cross-check (torch SDPA in float64, scipy logsumexp)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,W,seq", [(False, -1, False), (True, -1, False),
+                                           (True, 64, False), (False, -1, True),
+                                           (True, 100, True)])
+def test_matches_torch_sdpa_and_scipy_logsumexp(causal, W, seq):
+    p = workloads.make_prefill(31, 2, 150, 150, 6, 3, 32, "bf16", causal=causal,
+                               window_left=W, seqlens_k_range=(90, 150) if seq else None)
+    q, k, v = _f64(p)
+    o, lse = oracle.attention(q, k, v, scale=p.scale, causal=causal, window_left=W,
+                              seqlens_k=p.seqlens_k)
+    B, N, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    for b in range(B):
+        Lk = N if p.seqlens_k is None else int(p.seqlens_k[b])
+        # mask written independently from the definitions, as torch booleans
+        i = torch.arange(N)[:, None]
+        j = torch.arange(N)[None, :]
+        pos = i + (Lk - N)
+        mask = (j < Lk) & (i >= 0)                               # [N, N]
+        if causal:
+            mask = mask & (j <= pos)
+        if W > 0:
+            mask = mask & (j > pos - W)
+        qt = torch.from_numpy(q[b]).permute(1, 0, 2)                      # [H, N, d]
+        kt = torch.from_numpy(k[b]).permute(1, 0, 2).repeat_interleave(G, 0)
+        vt = torch.from_numpy(v[b]).permute(1, 0, 2).repeat_interleave(G, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=mask, scale=float(np.float32(p.scale)))
+        rows = mask.any(dim=1).numpy()
+        np.testing.assert_allclose(o[b][rows], ref.permute(1, 0, 2).numpy()[rows],
+                                   rtol=0, atol=1e-12)
+        s = float(np.float32(p.scale)) * torch.einsum("hnd,hmd->hnm", qt, kt).numpy()
+        s = np.where(mask.numpy()[None], s, -np.inf)
+        ref_lse = scipy.special.logsumexp(s, axis=-1)
+        np.testing.assert_allclose(lse[b][:, rows], ref_lse[:, rows], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P10: the blockwise online recurrence and the split-KV combine rule reach
+# the three-step result (fp64)
+# ---------------------------------------------------------------------------
+def _online(qr, k, v, scale, vis, block):
+    n, d = qr.shape
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, d))
+    for j0 in range(0, k.shape[0], block):
+        s = scale * (qr @ k[j0:j0 + block].T)
+        s = np.where(vis[:, j0:j0 + block], s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        ref = np.where(np.isfinite(m_new), m_new, 0.0)
+        alpha = np.exp(m - ref)
+        pblk = np.exp(s - ref[:, None])
+        l = alpha * l + pblk.sum(axis=1)
+        acc = alpha[:, None] * acc + pblk @ v[j0:j0 + block]
+        m = m_new
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = np.where(l[:, None] > 0, acc / l[:, None], 0.0)
+        lse = np.where(l > 0, m + np.log(l), -np.inf)
+    return o, lse
+
+
+@pytest.mark.parametrize("block", [1, 7, 64, 128, 300])
+def test_online_recurrence_matches_three_step(block):
+    rng = np.random.default_rng(12)
+    N, d = 300, 16
+    q = rng.standard_normal((N, d)) * 2
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    scale = 0.25
+    vis = oracle.visible_matrix(np.arange(N), N, 290, 271, True, 50)
+    o_ref, l_ref = oracle.attention(q[None, :, None], k[None, :, None], v[None, :, None],
+                                    scale=scale, causal=True, window_left=50,
+                                    seqlens_q=[290], seqlens_k=[271])
+    o, lse = _online(q, k, v, float(np.float32(scale)), vis, block)
+    np.testing.assert_allclose(o, o_ref[0, :, 0], rtol=0, atol=1e-12)
+    fin = np.isfinite(l_ref[0, 0])
+    np.testing.assert_array_equal(np.isfinite(lse), fin)
+    np.testing.assert_allclose(lse[fin], l_ref[0, 0][fin], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [1, 33, 256, 1000])
+def test_split_kv_combine_matches_decode(chunk):
+    """Partial (O~, m, l) per key chunk, merged by max/exp-weighted sums."""
+    prob = workloads.make_decode(41, 3, 8, 2, 16, 700, (1, 700), "f32")
+    q = workloads.to_f64(prob.q, "f32")
+    kc = workloads.to_f64(prob.k_cache, "f32")
+    vc = workloads.to_f64(prob.v_cache, "f32")
+    o_ref, l_ref = oracle.decode(q, kc, vc, prob.seqlens_k, scale=prob.scale)
+    sc = float(np.float32(prob.scale))
+    for b in range(3):
+        L = int(prob.seqlens_k[b])
+        for h in range(8):
+            parts = []
+            for c0 in range(0, L, chunk):
+                s = sc * (kc[b, c0:c0 + chunk][:L - c0, h // 4] @ q[b, h])
+                m = s.max()
+                p = np.exp(s - m)
+                parts.append((m, p.sum(), p @ vc[b, c0:c0 + chunk][:L - c0, h // 4]))
+            M = max(m for m, _, _ in parts)
+            Lsum = sum(np.exp(m - M) * l for m, l, _ in parts)
+            O = sum(np.exp(m - M) * ot for m, _, ot in parts) / Lsum
+            np.testing.assert_allclose(O, o_ref[b, h], atol=1e-12)
+            assert abs(M + math.log(Lsum) - l_ref[b, h]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Decode-specific pins
+# ---------------------------------------------------------------------------
+def test_decode_closed_forms_and_poison():
+    prob = workloads.make_decode(42, 4, 4, 2, 8, 64, (1, 64), "bf16",
+                                 lengths=np.array([1, 17, 64, 0], dtype=np.int32))
+    q = np.zeros((4, 4, 8))
+    kc = workloads.to_f64(prob.k_cache, "bf16")
+    vc = workloads.to_f64(prob.v_cache, "bf16")
+    assert np.isnan(kc[0, 1:]).all()                 # poisoned tail is present
+    o, lse = oracle.decode(q, kc, vc, prob.seqlens_k, scale=prob.scale)
+    for b, L in enumerate([1, 17, 64, 0]):
+        for h in range(4):
+            if L == 0:
+                assert np.all(o[b, h] == 0) and lse[b, h] == -np.inf
+                continue
+            np.testing.assert_allclose(o[b, h], vc[b, :L, h // 2].mean(axis=0), atol=1e-12)
+            assert abs(lse[b, h] - math.log(L)) < 1e-12
+    # L = 1 returns V[0] exactly for any query
+    qr = workloads.to_f64(prob.q, "bf16")
+    o1, _ = oracle.decode(qr, kc, vc, prob.seqlens_k, scale=prob.scale)
+    assert np.array_equal(o1[0, 1], vc[0, 0, 0])
+    # window W keeps the last W keys
+    o2, l2 = oracle.decode(q, kc, vc, prob.seqlens_k, scale=prob.scale, window_left=5)
+    np.testing.assert_allclose(o2[2, 0], vc[2, 59:64, 0].mean(axis=0), atol=1e-12)
+    assert abs(l2[2, 0] - math.log(5)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Hand-derived fixtures (closed forms with their derivations)
+# ---------------------------------------------------------------------------
+def test_golden_closed_forms():
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        cases = json.load(f)["cases"]
+    assert len(cases) >= 3
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float64)
+        k = np.array(c["k"], dtype=np.float64)
+        v = np.array(c["v"], dtype=np.float64)
+        o, lse = oracle.attention(q[None, :, None], k[None, :, None], v[None, :, None],
+                                  scale=c["scale"], causal=c["causal"],
+                                  window_left=c.get("window_left", -1))
+        np.testing.assert_allclose(o[0, :, 0], np.array(c["expect_o"]), rtol=0,
+                                   atol=1e-12, err_msg=c["name"])
+        exp_lse = [(-math.inf if x is None else x) for x in c["expect_lse"]]
+        np.testing.assert_allclose(lse[0, 0], exp_lse, rtol=0, atol=1e-12,
+                                   err_msg=c["name"])
+
+
+# ---------------------------------------------------------------------------
+# Input generator: bf16 rounding and determinism
+# ---------------------------------------------------------------------------
+def test_bf16_round_to_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 65504.0, 1e-40],
+                    dtype=np.float32)
+    bits = workloads.f32_to_bf16_bits(vals)
+    assert bits[0] == 0x3F80 and bits[1] == 0x3F80 and bits[2] == 0x3F82
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 100
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(workloads.f32_to_bf16_bits(x), ref)
+    np.testing.assert_array_equal(workloads.bf16_bits_to_f32(ref),
+                                  torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16)
+                                  .float().numpy())
+
+
+def test_generator_hashes_are_stable():
+    with open(os.path.join(GOLDEN, "input_hashes.json")) as f:
+        stored = json.load(f)
+    p = workloads.make_workload(1)
+    assert p.sha256() == stored["workload_1"]
+    small = workloads.make_prefill(5, 2, 70, 70, 4, 2, 64, "bf16", causal=True,
+                                   seqlens_k_range=(1, 70))
+    assert small.sha256() == stored["prefill_small"]
+    dec = workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16")
+    assert dec.sha256() == stored["decode_small"]
