@@ -1,0 +1,216 @@
+"""Benchmark of the fused-attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  * prefill: causal attention, B=1, 32 heads, N=8192, d=128, bf16
+    (the 7B-decoder-shaped workload), one fa_prefill_fwd call;
+  * decode: B=64, Hq=32, Hkv=8, d=128, bf16, per-sequence KV lengths drawn
+    uniformly in [512, 8192] over a capacity-8192 cache, one fa_decode_fwd
+    call (split + combine kernels).
+Inputs are generated once (seeded), copied to HBM, and the timed region only
+enqueues library calls.  Each call is bracketed by HIP events on the stream
+it is launched on (torch's current stream, which the binding passes to the
+library), so the per-call averages are kernel time plus launch gaps.
+
+Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
+algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
+decode throughput is reported beside it in GB/s on algorithmic bytes (each
+valid K and V row read once per GQA group, plus Q, O, LSE, lengths).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def prefill_flops(B, H, N, d):
+    return 4.0 * d * H * B * N * (N + 1) / 2.0
+
+
+def decode_bytes(seqlens, Hq, Hkv, d, elt=2):
+    kv = float(np.sum(seqlens)) * Hkv * d * elt * 2
+    q_o = 2.0 * len(seqlens) * Hq * d * elt
+    return kv + q_o + len(seqlens) * Hq * 4 + len(seqlens) * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (used for profiler runs)")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="heads of the prefill workload the CPU oracle times")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def to_dev(a, dtype, torch, dev):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def cpu_baseline(p, heads):
+    """Time the fp64 oracle on a bounded sample of the prefill workload."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    q = workloads.to_f64(p.q[:, :, :heads], "bf16")
+    k = workloads.to_f64(p.k[:, :, :heads], "bf16")
+    v = workloads.to_f64(p.v[:, :, :heads], "bf16")
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, scale=p.scale, causal=True)
+    dt = time.perf_counter() - t0
+    B, N = p.q.shape[0], p.q.shape[1]
+    flops = prefill_flops(B, heads, N, p.q.shape[3])
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 NumPy three-step oracle on {heads} of 32 heads of the causal "
+                      f"N=8192 d=128 prefill (all rows), {dt:.2f} s wall, {cpu}, "
+                      f"affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_flashattention_amd as fa
+    import workloads
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
+
+    # ---- inputs (seeded, generated once, resident in HBM) ------------------
+    p = workloads.make_workload(3)
+    B, N, H, d = p.q.shape
+    q, k, v = (to_dev(x, "bf16", torch, dev) for x in (p.q, p.k, p.v))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    dp = workloads.make_workload(5)
+    Bd, Hq, dd = dp.q.shape
+    Hkv = dp.k_cache.shape[2]
+    qd, kc, vc = (to_dev(x, "bf16", torch, dev) for x in (dp.q, dp.k_cache, dp.v_cache))
+    sk = torch.from_numpy(dp.seqlens_k).to(dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((Bd, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_size(qd, kc, vc), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        fa.decode(qd, kc, vc, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    flops = prefill_flops(B, H, N, d)
+    tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
+    dbytes = decode_bytes(dp.seqlens_k, Hq, Hkv, dd)
+    gbs = dbytes / (dec_ms.mean() * 1e-3) / 1e9
+
+    result = {
+        "metric": "attention fwd TFLOP/s (causal N=8192,d=128) + decode HBM GB/s, % of roofline",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill B1 H32 N8192 d128 bf16 + decode B64 Hq32 Hkv8 d128 "
+                        "bf16 KV lengths U[512,8192]",
+            "prefill": {"batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": True},
+            "decode": {"batch": Bd, "heads_q": Hq, "heads_kv": Hkv, "head_dim": dd,
+                       "capacity": int(dp.k_cache.shape[1]),
+                       "sum_kv_len": int(np.sum(dp.seqlens_k))},
+            "parallelism": "single GPU",
+        },
+        "prefill": {"ms_mean": round(float(pre_ms.mean()), 4),
+                    "ms_median": round(float(np.median(pre_ms)), 4),
+                    "ms_min": round(float(pre_ms.min()), 4),
+                    "algorithmic_flop": flops},
+        "decode": {"value": round(gbs, 1), "unit": "GB/s",
+                   "ms_mean": round(float(dec_ms.mean()), 4),
+                   "ms_median": round(float(np.median(dec_ms)), 4),
+                   "ms_min": round(float(dec_ms.min()), 4),
+                   "algorithmic_bytes": dbytes},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": None},
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * fa.h -- C ABI of the fused-attention library for AMD Instinct MI355X
+ * (gfx950).  Plain C: callers need neither HIP nor PyTorch headers.
+ *
+ * The library computes scaled dot-product attention
+ *
+ *     O = softmax(scale * Q K^T + mask) V,    LSE_i = ln sum_j exp(scale * q_i . k_j)
+ *
+ * (the attention definition of the ops-transformer practice page on
+ * jsqmd.com, section 二 "SelfAttention baseline and its bottleneck") in one
+ * fused pass per query tile with a running max / running sum softmax, so the
+ * N x N score matrix never reaches device memory (same page, section 二
+ * "fused computation idea"; hwcomputing.csdn.net page, sections 2.1-2.2).
+ * The sum in LSE runs over visible keys only, in natural log.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or keeps device memory between calls.
+ * - Strides are in ELEMENTS, not bytes; the innermost (head_dim) stride is 1.
+ * - Calls are asynchronous: kernels are enqueued on `hip_stream` (a
+ *   hipStream_t passed as void*; NULL = the default stream).  Results are
+ *   ready once that stream is synchronised.  Faults inside a kernel surface
+ *   at that synchronisation, not as a return code.
+ * - Every argument check runs before any HIP call.  A failing check returns
+ *   FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED and leaves the outputs
+ *   untouched; fa_last_error_message() then describes the problem.
+ * - A batch of 0, or a zero query extent, is a valid no-op (FA_OK).
+ * - The library has no global state; concurrent calls on different streams
+ *   are safe.  The error message buffer is thread-local.
+ * - Masking is implicit (no mask tensor is read): the causal mask is applied
+ *   by index arithmetic inside the kernel and fully masked tiles are skipped
+ *   (jsqmd.com page, section 二 "causal mask and decode"); padding beyond a
+ *   valid length is never read (agent.csdn.net BERT page, chapter 四: tiles
+ *   whose length is not a multiple of the tile size must not read out of
+ *   bounds).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,   /* NULL pointer, bad extent, bad stride, bad scale ... */
+    FA_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement   */
+    FA_ERR_WORKSPACE = 3,     /* decode workspace missing or too small              */
+    FA_ERR_HIP = 4            /* the HIP runtime reported an error at launch        */
+} fa_status;
+
+typedef enum {
+    FA_DTYPE_F32 = 0,         /* fp32 in, fp32 products and accumulation, fp32 out  */
+    FA_DTYPE_BF16 = 1         /* bf16 in, bf16 MFMA with fp32 accumulation, bf16 out */
+} fa_dtype;
+
+/*
+ * Prefill / encoder attention: fa_prefill_fwd
+ * -------------------------------------------
+ * Mirrors the fused-operator calls of the pages: flash_attention(query, key,
+ * value, causal, softmax_scale) (jsqmd.com page, sections 一 and 二) and
+ * flash_attention_score(..., actual_seq_q, actual_seq_kv) with valid lengths
+ * instead of a padding mask (agent.csdn.net BERT page, chapter 三 and its
+ * closing section on variable-length batches).  Dropout (keep_prob) is not
+ * part of the operation.
+ *
+ * Layout: BSHD by default, [batch, seq, head, dim] (the (N, S, D) input
+ * layout of the BERT page, chapter 四), but any layout with a unit dim
+ * stride is accepted through the three strides (batch, seq, head); a packed
+ * QKV buffer is expressed with three base pointers sharing one seq stride.
+ *   q : [batch, seqlen_q, heads_q,  head_dim]
+ *   k : [batch, seqlen_k, heads_kv, head_dim]
+ *   v : [batch, seqlen_k, heads_kv, head_dim]
+ *   o : [batch, seqlen_q, heads_q,  head_dim]   (written; same dtype as q)
+ *   lse: contiguous fp32 [batch, heads_q, seqlen_q] (written), or NULL to skip.
+ *
+ * Visibility of key j to query row i of sequence b, with Lq = seqlens_q[b]
+ * (or seqlen_q when NULL) and Lk = seqlens_k[b] (or seqlen_k when NULL),
+ * each clamped to [0, extent]:
+ *   i < Lq  and  j < Lk
+ *   causal:          j <= i + (Lk - Lq)          (bottom-right aligned)
+ *   window_left W>0: j >  i + (Lk - Lq) - W      (W keys including the diagonal)
+ * A row with no visible key gets O = 0 and LSE = -inf; rows i >= Lq are
+ * written as O = 0, LSE = -inf.  Query head h reads key/value head
+ * h / (heads_q / heads_kv) (grouped-query attention; MQA when heads_kv = 1).
+ *
+ * Requirements: head_dim in {64, 128}; heads_q % heads_kv == 0;
+ * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
+ * window_left == -1 or >= 1; extents >= 0; seqlens arrays (if given) are
+ * device int32 [batch].  Pointers must be 16-byte aligned and strides of
+ * batch/seq/head multiples of 8 elements (bf16) or 4 elements (fp32).
+ */
+typedef struct {
+    int32_t dtype;                       /* fa_dtype; q, k, v and o share it     */
+    int32_t batch;
+    int32_t seqlen_q;                    /* padded query extent                  */
+    int32_t seqlen_k;                    /* padded key/value extent              */
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t head_dim;
+    int32_t causal;                      /* 0 or 1                               */
+    int32_t window_left;                 /* -1 = none, else W >= 1               */
+    float softmax_scale;                 /* multiplier on Q K^T                  */
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;                          /* may be NULL                          */
+    const int32_t *seqlens_q;            /* device [batch] or NULL               */
+    const int32_t *seqlens_k;            /* device [batch] or NULL               */
+    int64_t q_stride[3];                 /* batch, seq, head (elements)          */
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+} fa_prefill_params;
+
+/*
+ * Single-token decode over a KV cache: fa_decode_workspace_size, fa_decode_fwd
+ * ---------------------------------------------------------------------------
+ * The incremental mode of the BERT page's closing section: the new token's
+ * query attends to every cached key/value of its sequence; cached entries
+ * are not recomputed.  The caller has already appended the current token's
+ * K and V, so sequence b attends to cache rows 0 .. L_b-1 with
+ * L_b = seqlens_k[b] clamped to [0, cache_capacity] (device int32 [batch],
+ * required).  With window_left = W >= 1 only rows j > L_b - 1 - W are read.
+ *   q       : [batch, heads_q, head_dim]          via q_stride (batch, head)
+ *   k_cache : [batch, capacity, heads_kv, head_dim] via k_stride (batch, seq, head)
+ *   v_cache : same shape, via v_stride
+ *   o       : [batch, heads_q, head_dim]          via o_stride (batch, head)
+ *   lse     : contiguous fp32 [batch, heads_q], or NULL.
+ * Cache rows at or beyond L_b are never read, so they may hold anything.
+ * The kernels split each sequence's keys into chunks (split-KV), read every
+ * K/V row once for all heads_q / heads_kv query heads of its group, and merge
+ * the per-chunk partial results with a log-sum-exp combine pass.
+ *
+ * chunk_keys: 0 lets the library choose; otherwise 64, 128 or 256.  Results
+ * agree to rounding for every choice.
+ *
+ * Workspace: fa_decode_workspace_size() reports the bytes fa_decode_fwd needs
+ * for this parameter set (it depends on batch, heads, head_dim, capacity and
+ * the chunk size only, never on device data).  The caller allocates it
+ * (device memory, 16-byte aligned) and passes it in; its contents need no
+ * initialisation and are scratch after the call.  Two calls that overlap in
+ * time must not share one workspace.
+ *
+ * Requirements: dtype FA_DTYPE_BF16; head_dim in {64, 128};
+ * heads_q % heads_kv == 0; cache_capacity >= 1; softmax_scale finite and > 0.
+ */
+typedef struct {
+    int32_t dtype;                       /* fa_dtype (bf16 only)                 */
+    int32_t batch;
+    int32_t heads_q;
+    int32_t heads_kv;
+    int32_t head_dim;
+    int32_t cache_capacity;              /* rows allocated per sequence          */
+    int32_t window_left;                 /* -1 = none, else W >= 1               */
+    int32_t chunk_keys;                  /* 0 = library choice, or 64/128/256    */
+    float softmax_scale;
+    int32_t reserved0;                   /* must be 0                            */
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    void *o;
+    float *lse;                          /* may be NULL                          */
+    const int32_t *seqlens_k;            /* device [batch], required             */
+    int64_t q_stride[2];                 /* batch, head (elements)               */
+    int64_t k_stride[3];                 /* batch, seq, head                     */
+    int64_t v_stride[3];
+    int64_t o_stride[2];                 /* batch, head                          */
+} fa_decode_params;
+
+/* Enqueue the prefill forward pass.  Returns FA_OK, FA_ERR_INVALID_ARG,
+ * FA_ERR_UNSUPPORTED or FA_ERR_HIP (launch failure). */
+fa_status fa_prefill_fwd(const fa_prefill_params *params, void *hip_stream);
+
+/* Bytes of device workspace fa_decode_fwd needs for `params` (host-only
+ * computation; no HIP call).  Writes *bytes and returns FA_OK, or returns an
+ * argument error without writing. */
+fa_status fa_decode_workspace_size(const fa_decode_params *params, size_t *bytes);
+
+/* Enqueue the split-KV decode (two kernels on `hip_stream`).  Returns FA_OK,
+ * FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE (NULL workspace or
+ * workspace_bytes below fa_decode_workspace_size) or FA_ERR_HIP. */
+fa_status fa_decode_fwd(const fa_decode_params *params, void *workspace,
+                        size_t workspace_bytes, void *hip_stream);
+
+/* Static string naming a status code (never NULL). */
+const char *fa_status_str(fa_status status);
+
+/* Thread-local description of the last non-OK return on this thread
+ * ("" if none).  Valid until the next library call on the same thread. */
+const char *fa_last_error_message(void);
+
+/* ABI version of this header: major * 10000 + minor * 100 + patch. */
+int32_t fa_abi_version(void);
+
+#define FA_ABI_VERSION 10000
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,232 @@
+"""C-ABI checks that need no GPU.
+
+* the shared library loads and exports every function ``include/fa.h``
+  declares;
+* the ctypes structs match the C layout (sizes and offsets from a program
+  compiled with gcc against the header);
+* every argument check returns its status and message before any HIP call
+  (none of these cases reaches a launch);
+* the decode workspace size is a host-side formula.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from transformer_attention_flashattention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfa.so is not built: run __graft_entry__.build() first")
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_abi_version_and_status_strings(lib):
+    m = re.search(r"#define FA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.fa_abi_version() == int(m.group(1))
+    names = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED",
+             3: "FA_ERR_WORKSPACE", 4: "FA_ERR_HIP"}
+    for code, name in names.items():
+        assert _lib.status_str(code) == name
+    assert _lib.status_str(99) == "FA_ERR_UNKNOWN"
+
+
+LAYOUT_PROG = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "fa.h"
+#define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("prefill %zu\n", sizeof(fa_prefill_params));
+  printf("decode %zu\n", sizeof(fa_decode_params));
+  F(fa_prefill_params, softmax_scale) F(fa_prefill_params, q) F(fa_prefill_params, lse)
+  F(fa_prefill_params, seqlens_k) F(fa_prefill_params, q_stride) F(fa_prefill_params, o_stride)
+  F(fa_decode_params, softmax_scale) F(fa_decode_params, reserved0) F(fa_decode_params, q)
+  F(fa_decode_params, seqlens_k) F(fa_decode_params, q_stride) F(fa_decode_params, k_stride)
+  F(fa_decode_params, o_stride)
+  return 0;
+}
+"""
+
+
+def test_struct_layout_matches_c():
+    with tempfile.TemporaryDirectory() as td:
+        src = os.path.join(td, "layout.c")
+        exe = os.path.join(td, "layout")
+        open(src, "w").write(LAYOUT_PROG)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-I", os.path.join(ROOT, "include"), src,
+                        "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    vals = dict(line.rsplit(" ", 1) for line in out.splitlines())
+    assert int(vals["prefill"]) == ctypes.sizeof(_lib.PrefillParams)
+    assert int(vals["decode"]) == ctypes.sizeof(_lib.DecodeParams)
+    for key, v in vals.items():
+        if "." not in key:
+            continue
+        struct, field = key.split(".")
+        cls = _lib.PrefillParams if struct == "fa_prefill_params" else _lib.DecodeParams
+        assert getattr(cls, field).offset == int(v), key
+
+
+# ---------------------------------------------------------------------------
+# Validation: each case must fail on the host, before any HIP call.
+# Pointers are fake (never dereferenced) but 16-byte aligned unless the case
+# is about alignment.
+# ---------------------------------------------------------------------------
+FAKE = 0x10000
+
+
+def _prefill(**kw):
+    p = _lib.PrefillParams()
+    p.dtype = _lib.FA_DTYPE_BF16
+    p.batch, p.seqlen_q, p.seqlen_k = 2, 100, 100
+    p.heads_q, p.heads_kv, p.head_dim = 8, 2, 128
+    p.causal, p.window_left, p.softmax_scale = 1, -1, 0.088
+    p.q, p.k, p.v, p.o, p.lse = FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384
+    st = [100 * 8 * 128, 8 * 128, 128]
+    stk = [100 * 2 * 128, 2 * 128, 128]
+    p.q_stride[:] = st
+    p.k_stride[:] = stk
+    p.v_stride[:] = stk
+    p.o_stride[:] = st
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(p, k)[:] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=7), _lib.FA_ERR_INVALID_ARG, "dtype"),
+    (dict(batch=-1), _lib.FA_ERR_INVALID_ARG, "batch"),
+    (dict(heads_kv=3), _lib.FA_ERR_INVALID_ARG, "multiple"),
+    (dict(heads_q=0), _lib.FA_ERR_INVALID_ARG, "heads"),
+    (dict(head_dim=96), _lib.FA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(window_left=0), _lib.FA_ERR_INVALID_ARG, "window"),
+    (dict(window_left=-5), _lib.FA_ERR_INVALID_ARG, "window"),
+    (dict(causal=2), _lib.FA_ERR_INVALID_ARG, "causal"),
+    (dict(softmax_scale=0.0), _lib.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(softmax_scale=float("nan")), _lib.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(softmax_scale=-0.1), _lib.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(q_stride=[100 * 8 * 128, 8 * 128, 130]), _lib.FA_ERR_UNSUPPORTED, "q_stride"),
+    (dict(k_stride=[-1, 256, 128]), _lib.FA_ERR_INVALID_ARG, "k_stride"),
+    (dict(q=None), _lib.FA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(v=None), _lib.FA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(o=FAKE + 2), _lib.FA_ERR_UNSUPPORTED, "aligned"),
+])
+def test_prefill_validation(lib, kw, status, needle):
+    p = _prefill(**kw)
+    st = _lib.prefill_fwd(p, 0)
+    assert st == status, (_lib.status_str(st), _lib.last_error())
+    assert needle in _lib.last_error()
+
+
+def test_prefill_fp32_stride_rule(lib):
+    # fp32 needs strides in multiples of 4 elements, bf16 in multiples of 8
+    p = _prefill(dtype=_lib.FA_DTYPE_F32, q_stride=[100 * 8 * 128, 8 * 128, 130])
+    assert _lib.prefill_fwd(p, 0) == _lib.FA_ERR_UNSUPPORTED
+    p = _prefill(dtype=_lib.FA_DTYPE_F32, q_stride=[100 * 8 * 128, 8 * 128, 132], q=None)
+    assert _lib.prefill_fwd(p, 0) == _lib.FA_ERR_INVALID_ARG
+    p = _prefill(dtype=_lib.FA_DTYPE_BF16, q_stride=[100 * 8 * 128, 8 * 128, 132])
+    assert _lib.prefill_fwd(p, 0) == _lib.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(seqlen_q=0)])
+def test_prefill_empty_is_noop(lib, kw):
+    # no launch happens for an empty problem, so fake pointers are fine
+    p = _prefill(**kw)
+    assert _lib.prefill_fwd(p, 0) == _lib.FA_OK
+    assert _lib.last_error() == ""
+
+
+def _decode(**kw):
+    p = _lib.DecodeParams()
+    p.dtype = _lib.FA_DTYPE_BF16
+    p.batch, p.heads_q, p.heads_kv, p.head_dim = 64, 32, 8, 128
+    p.cache_capacity, p.window_left, p.chunk_keys = 8192, -1, 0
+    p.softmax_scale, p.reserved0 = 0.088, 0
+    p.q, p.k_cache, p.v_cache, p.o, p.lse, p.seqlens_k = (FAKE, FAKE + 4096, FAKE + 8192,
+                                                          FAKE + 12288, FAKE + 16384, FAKE + 20480)
+    p.q_stride[:] = [32 * 128, 128]
+    p.k_stride[:] = [8192 * 8 * 128, 8 * 128, 128]
+    p.v_stride[:] = [8192 * 8 * 128, 8 * 128, 128]
+    p.o_stride[:] = [32 * 128, 128]
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            getattr(p, k)[:] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=_lib.FA_DTYPE_F32), _lib.FA_ERR_UNSUPPORTED, "bf16"),
+    (dict(dtype=3), _lib.FA_ERR_INVALID_ARG, "dtype"),
+    (dict(heads_kv=5), _lib.FA_ERR_INVALID_ARG, "multiple"),
+    (dict(head_dim=80), _lib.FA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(cache_capacity=0), _lib.FA_ERR_INVALID_ARG, "capacity"),
+    (dict(window_left=0), _lib.FA_ERR_INVALID_ARG, "window"),
+    (dict(chunk_keys=100), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
+    (dict(reserved0=1), _lib.FA_ERR_INVALID_ARG, "reserved0"),
+    (dict(softmax_scale=float("inf")), _lib.FA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(seqlens_k=None), _lib.FA_ERR_INVALID_ARG, "seqlens_k"),
+    (dict(k_cache=FAKE + 8), _lib.FA_ERR_UNSUPPORTED, "aligned"),
+    (dict(k_stride=[8192 * 8 * 128, 8 * 128, 132]), _lib.FA_ERR_UNSUPPORTED, "k_stride"),
+])
+def test_decode_validation(lib, kw, status, needle):
+    p = _decode(**kw)
+    st = _lib.decode_fwd(p, FAKE, 1 << 40, 0)
+    assert st == status, (_lib.status_str(st), _lib.last_error())
+    assert needle in _lib.last_error()
+    st2, _ = _lib.decode_workspace_size(p)
+    assert st2 == status
+
+
+def test_decode_workspace_rules(lib):
+    p = _decode()
+    st, n = _lib.decode_workspace_size(p)
+    assert st == _lib.FA_OK
+    # library choice at this size is 256-key chunks: 32 chunks of 64*32 rows
+    rows = 64 * 32 * 32
+    expect = ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    assert n == expect
+    assert _lib.decode_fwd(p, None, n, 0) == _lib.FA_ERR_WORKSPACE
+    assert "NULL" in _lib.last_error()
+    assert _lib.decode_fwd(p, FAKE, n - 1, 0) == _lib.FA_ERR_WORKSPACE
+    assert "too small" in _lib.last_error()
+    assert _lib.decode_fwd(p, FAKE + 4, n, 0) == _lib.FA_ERR_WORKSPACE
+    # explicit chunk sizes change the requirement accordingly
+    p64 = _decode(chunk_keys=64)
+    _, n64 = _lib.decode_workspace_size(p64)
+    rows = 64 * 32 * 128
+    assert n64 == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    # empty batch is a no-op needing no workspace
+    p0 = _decode(batch=0)
+    assert _lib.decode_workspace_size(p0) == (_lib.FA_OK, 0)
+    assert _lib.decode_fwd(p0, None, 0, 0) == _lib.FA_OK

@@ -1,0 +1,115 @@
+"""GPU parity: fa_decode_fwd (split-KV decode + LSE combine, through the C
+ABI) against the fp64 oracle.  Caches come from the generator with every row
+at or beyond a sequence's length set to NaN, so any read past the valid
+prefix would poison the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import transformer_attention_flashattention_amd as fa
+import workloads
+from gpu_helpers import (DEV, check, decode_inputs, dev_tensor, oracle_decode, run_decode, say,
+                         to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(dp, ctx, **kw):
+    say(f"[decode] {ctx} B={dp.q.shape[0]} Hq={dp.q.shape[1]} Hkv={dp.k_cache.shape[2]} "
+        f"d={dp.q.shape[2]} cap={dp.k_cache.shape[1]} W={dp.window_left} {kw}")
+    o, lse = run_decode(dp, **kw)
+    ro, rl = oracle_decode(dp)
+    check(o, lse, ro, rl, dp.dtype, ctx)
+    return o, lse
+
+
+def test_workload5_decode_full():
+    _case(workloads.make_workload(5), "decode B64 Hq32 Hkv8 d128 L U[512,8192]")
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 128, 256])
+def test_lengths_around_chunk_edges(chunk):
+    lengths = np.array([1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 600, 0, 1000],
+                       dtype=np.int32)
+    dp = workloads.make_decode(50, len(lengths), 8, 2, 128, 1000, (1, 1000), "bf16",
+                               lengths=lengths)
+    _case(dp, f"lengths at chunk edges, chunk={chunk}", chunk_keys=chunk)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (6, 2), (8, 1), (12, 4)])
+def test_gqa_groups(Hq, Hkv):
+    dp = workloads.make_decode(51 + Hq, 5, Hq, Hkv, 128, 900, (1, 900), "bf16")
+    _case(dp, f"GQA Hq{Hq} Hkv{Hkv}")
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 256])
+def test_head_dim_64(chunk):
+    dp = workloads.make_decode(52, 6, 12, 4, 64, 777, (1, 777), "bf16")
+    _case(dp, "d64", chunk_keys=chunk)
+
+
+@pytest.mark.parametrize("W", [1, 64, 100, 5000])
+def test_window(W):
+    dp = workloads.make_decode(53, 6, 8, 2, 128, 1200, (1, 1200), "bf16", window_left=W)
+    _case(dp, f"window {W}")
+
+
+def test_lengths_clamped_to_capacity():
+    dp = workloads.make_decode(54, 3, 4, 2, 128, 300, (1, 300), "bf16")
+    q, kc, vc, sk = decode_inputs(dp)
+    big = torch.tensor([5000, -7, 300], dtype=torch.int32, device=DEV)
+    o, lse = fa.decode(q, kc, vc, big, scale=dp.scale)
+    torch.cuda.synchronize()
+    # reference with the clamped lengths; the oracle clamps the same way
+    dp.seqlens_k = np.array([5000, -7, 300], dtype=np.int32)
+    ro, rl = oracle_decode(dp)
+    check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "clamped lengths")
+
+
+def test_chunk_sizes_agree():
+    dp = workloads.make_decode(55, 8, 8, 2, 128, 2000, (1, 2000), "bf16")
+    outs = [run_decode(dp, chunk_keys=c) for c in (64, 128, 256)]
+    for o, l in outs[1:]:
+        assert np.abs(o - outs[0][0]).max() <= 2e-2
+        assert np.abs(l - outs[0][1]).max() <= 1e-3
+
+
+def test_decode_equals_single_query_prefill():
+    """The decode query is a one-row bottom-right-aligned causal prefill."""
+    dp = workloads.make_decode(56, 5, 8, 2, 128, 520, (1, 520), "bf16")
+    q, kc, vc, sk = decode_inputs(dp)
+    od, ld = fa.decode(q, kc, vc, sk, scale=dp.scale)
+    op, lp = fa.prefill(q[:, None], kc, vc, causal=True, scale=dp.scale,
+                        seqlens_q=torch.ones(5, dtype=torch.int32, device=DEV), seqlens_k=sk)
+    torch.cuda.synchronize()
+    assert np.abs(to_np(od) - to_np(op[:, 0])).max() <= 2e-2
+    assert np.abs(ld.cpu().numpy() - lp[:, :, 0].cpu().numpy()).max() <= 1e-3
+
+
+def test_run_to_run_bit_identical_and_workspace_reuse():
+    dp = workloads.make_decode(57, 4, 8, 2, 128, 700, (1, 700), "bf16")
+    q, kc, vc, sk = decode_inputs(dp)
+    ws = torch.empty(fa.decode_workspace_size(q, kc, vc), dtype=torch.uint8, device=DEV)
+    outs = [fa.decode(q, kc, vc, sk, scale=dp.scale, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+
+
+def test_no_writes_outside_outputs():
+    dp = workloads.make_decode(58, 3, 8, 2, 128, 400, (1, 400), "bf16")
+    q, kc, vc, sk = decode_inputs(dp)
+    pad = 2048
+    n = 3 * 8 * 128
+    o_buf = torch.full((n + 2 * pad,), 512.0, dtype=torch.bfloat16, device=DEV)
+    l_buf = torch.full((24 + 2 * pad,), 777.0, dtype=torch.float32, device=DEV)
+    o = o_buf[pad:pad + n].view(3, 8, 128)
+    lse = l_buf[pad:pad + 24].view(3, 8)
+    fa.decode(q, kc, vc, sk, scale=dp.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[:pad] == 512.0) and torch.all(o_buf[pad + n:] == 512.0)
+    assert torch.all(l_buf[:pad] == 777.0) and torch.all(l_buf[pad + 24:] == 777.0)
+    ro, rl = oracle_decode(dp)
+    check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "decode canaries")

@@ -1,0 +1,234 @@
+"""GPU parity: fa_prefill_fwd (through the C ABI) against the fp64 oracle.
+
+Small and medium problems are compared element by element on all outputs;
+the two full-size causal workloads (N = 8192 and the GQA window workload) are
+compared on sampled rows and heads, which the oracle computes one by one.
+Every case prints its name and shape before the GPU call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import transformer_attention_flashattention_amd as fa
+import workloads
+from gpu_helpers import DEV, check, dev_tensor, oracle_prefill, prefill_inputs, run_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(p, ctx):
+    say(f"[prefill] {ctx} shape(B,Nq,Nk,Hq,Hkv,d)={p.shape} dtype={p.dtype} causal={p.causal} "
+        f"W={p.window_left} seqlens_q={p.seqlens_q is not None} seqlens_k={p.seqlens_k is not None}")
+    o, lse = run_prefill(p)
+    ro, rl = oracle_prefill(p)
+    check(o, lse, ro, rl, p.dtype, ctx)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# The named workloads
+# ---------------------------------------------------------------------------
+def test_workload1_tiny_fp32():
+    _case(workloads.make_workload(1), "tiny fp32 B1 H1 N128 d64")
+
+
+def test_workload2_bert_varlen():
+    _case(workloads.make_workload(2), "BERT-base B8 H12 N512 d64 key lengths U[128,512]")
+
+
+def _sampled(p, ctx, rows, heads):
+    say(f"[prefill] {ctx} (full size, sampled rows) shape={p.shape}")
+    o, lse = run_prefill(p)
+    assert np.all(np.isfinite(o)), "non-finite output"
+    ro, rl = oracle_prefill(p, rows=rows, heads=heads)
+    check(o[:, rows][:, :, heads], lse[:, heads][:, :, rows], ro, rl, p.dtype, ctx)
+
+
+def test_workload3_causal_8k_sampled():
+    p = workloads.make_workload(3)
+    rng = np.random.default_rng(303)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 129, 4095, 4096, 8190, 8191],
+                                     rng.integers(0, 8192, 40)]))
+    heads = np.array([0, 5, 17, 31])
+    _sampled(p, "decoder-7B causal B1 H32 N8192 d128", rows, heads)
+
+
+def test_workload4_gqa_window_sampled():
+    p = workloads.make_workload(4)
+    rng = np.random.default_rng(404)
+    rows = np.unique(np.concatenate([[0, 1, 1023, 1024, 1025, 2047, 2048, 4095],
+                                     rng.integers(0, 4096, 40)]))
+    heads = np.array([0, 3, 4, 13, 31])
+    _sampled(p, "GQA causal window-1024 B2 Hq32 Hkv8 N4096 d128", rows, heads)
+
+
+# ---------------------------------------------------------------------------
+# Scaled-down versions of the full-size workloads, compared on every output
+# ---------------------------------------------------------------------------
+def test_causal_mha_medium_all_rows():
+    _case(workloads.make_prefill(33, 1, 1100, 1100, 4, 4, 128, "bf16", causal=True),
+          "causal MHA N1100 d128")
+
+
+def test_gqa_window_medium_all_rows():
+    _case(workloads.make_prefill(44, 2, 1000, 1000, 8, 2, 128, "bf16", causal=True,
+                                 window_left=256), "causal GQA window256 N1000 d128")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: ragged extents, windows, MQA, valid lengths, fp32 variants
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 65, 127, 129, 255, 509])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(N, causal):
+    _case(workloads.make_prefill(100 + N, 2, N, N, 4, 2, 128, "bf16", causal=causal),
+          f"ragged N{N} causal={causal}")
+
+
+@pytest.mark.parametrize("W", [1, 63, 64, 65, 200, 700])
+def test_causal_windows(W):
+    _case(workloads.make_prefill(200 + W, 1, 600, 600, 4, 2, 128, "bf16", causal=True,
+                                 window_left=W), f"causal window {W}")
+
+
+def test_window_without_causal():
+    _case(workloads.make_prefill(7, 2, 300, 300, 2, 2, 64, "bf16", window_left=100),
+          "window 100, not causal")
+
+
+def test_mqa_single_kv_head():
+    _case(workloads.make_prefill(8, 2, 257, 257, 8, 1, 128, "bf16", causal=True), "MQA Hkv=1")
+
+
+def test_head_dim_64_noncausal_gqa():
+    _case(workloads.make_prefill(9, 3, 333, 333, 6, 3, 64, "bf16"), "d64 GQA non-causal")
+
+
+def test_key_lengths_with_empty_and_single():
+    p = workloads.make_prefill(10, 4, 300, 300, 4, 4, 128, "bf16")
+    p.seqlens_k = np.array([0, 1, 77, 300], dtype=np.int32)
+    _case(p, "key lengths 0,1,77,300")
+
+
+def test_query_and_key_lengths():
+    p = workloads.make_prefill(11, 3, 400, 400, 4, 2, 128, "bf16", causal=True,
+                               seqlens_k_range=(1, 400), seqlens_q_equal_k=True)
+    _case(p, "q and k valid lengths, causal")
+
+
+def test_causal_fewer_keys_than_queries():
+    # bottom-right alignment: the first Lq - Lk rows see nothing
+    p = workloads.make_prefill(12, 2, 300, 300, 2, 2, 128, "bf16", causal=True)
+    p.seqlens_k = np.array([100, 299], dtype=np.int32)
+    _case(p, "causal with Lk < Lq")
+
+
+@pytest.mark.parametrize("Nq,Nk", [(100, 333), (333, 100), (64, 1000)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_cross_lengths(Nq, Nk, causal):
+    _case(workloads.make_prefill(13 + Nq, 2, Nq, Nk, 4, 2, 128, "bf16", causal=causal),
+          f"Nq{Nq} Nk{Nk} causal={causal}")
+
+
+@pytest.mark.parametrize("kw", [dict(causal=True), dict(causal=True, window_left=37),
+                                dict(seqlens_k_range=(1, 200)), dict()])
+def test_fp32_variants(kw):
+    _case(workloads.make_prefill(14, 2, 200, 200, 4, 2, 128, "f32", **kw), f"fp32 {kw}")
+    _case(workloads.make_prefill(15, 1, 130, 130, 2, 1, 64, "f32", **kw), f"fp32 d64 {kw}")
+
+
+def test_large_score_offset_is_stable():
+    """K -> K + u makes raw scores ~ +-100s; max subtraction keeps exp finite."""
+    p = workloads.make_prefill(16, 1, 300, 300, 2, 2, 128, "bf16", causal=True)
+    k = workloads.bf16_bits_to_f32(p.k) + np.float32(8.0)
+    p.k = workloads.f32_to_bf16_bits(k)
+    q = workloads.bf16_bits_to_f32(p.q) + np.float32(4.0)
+    p.q = workloads.f32_to_bf16_bits(q)
+    _case(p, "large score offsets")
+
+
+# ---------------------------------------------------------------------------
+# Padding, poisoning, canaries, determinism, layouts, memory
+# ---------------------------------------------------------------------------
+def test_poisoned_padding_matches_unpadded_prefix():
+    p = workloads.make_prefill(17, 3, 300, 300, 4, 2, 128, "bf16", causal=True,
+                               seqlens_k_range=(1, 300), seqlens_q_equal_k=True,
+                               poison_padding=True)
+    o, lse = _case(p, "NaN-poisoned padding")
+    for b in range(3):
+        L = int(p.seqlens_k[b])
+        sub = workloads.PrefillProblem("bf16", p.q[b:b + 1, :L].copy(), p.k[b:b + 1, :L].copy(),
+                                       p.v[b:b + 1, :L].copy(), p.scale, True)
+        o2, l2 = run_prefill(sub)
+        # same kernel, same tiles over the valid prefix: identical bits
+        assert np.array_equal(o[b:b + 1, :L], o2)
+        assert np.array_equal(lse[b:b + 1, :, :L], l2)
+
+
+def test_no_writes_outside_outputs():
+    p = workloads.make_prefill(18, 2, 130, 130, 4, 2, 128, "bf16", causal=True)
+    q, k, v, _, _ = prefill_inputs(p)
+    n_o = q.numel()
+    pad = 4096
+    o_buf = torch.full((n_o + 2 * pad,), 512.0, dtype=torch.bfloat16, device=DEV)
+    l_buf = torch.full((2 * 4 * 130 + 2 * pad,), 777.0, dtype=torch.float32, device=DEV)
+    o = o_buf[pad:pad + n_o].view(q.shape)
+    lse = l_buf[pad:pad + 2 * 4 * 130].view(2, 4, 130)
+    fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[:pad] == 512.0) and torch.all(o_buf[pad + n_o:] == 512.0)
+    assert torch.all(l_buf[:pad] == 777.0) and torch.all(l_buf[pad + 2 * 4 * 130:] == 777.0)
+    ro, rl = oracle_prefill(p)
+    check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+          ro, rl, "bf16", "canaries")
+
+
+def test_run_to_run_bit_identical():
+    p = workloads.make_prefill(19, 2, 700, 700, 8, 2, 128, "bf16", causal=True, window_left=300)
+    q, k, v, _, _ = prefill_inputs(p)
+    outs = [fa.prefill(q, k, v, causal=True, window=300, scale=p.scale) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+
+
+def test_strided_layouts_bhsd_and_packed_qkv():
+    p = workloads.make_prefill(20, 2, 200, 200, 4, 4, 128, "bf16", causal=True)
+    ro, rl = oracle_prefill(p)
+    q, k, v, _, _ = prefill_inputs(p)
+    # BHSD storage viewed as BSHD
+    qb, kb, vb = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
+    o, lse = fa.prefill(qb, kb, vb, causal=True, scale=p.scale)
+    torch.cuda.synchronize()
+    check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+          ro, rl, "bf16", "BHSD strides")
+    # one packed [B, N, 3, H, d] buffer
+    qkv = torch.stack([q, k, v], dim=2).contiguous()
+    o2, lse2 = fa.prefill(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], causal=True, scale=p.scale)
+    torch.cuda.synchronize()
+    check(o2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64),
+          ro, rl, "bf16", "packed QKV")
+
+
+def test_no_device_allocation_and_optional_lse():
+    p = workloads.make_prefill(21, 1, 512, 512, 4, 4, 128, "bf16", causal=True)
+    q, k, v, _, _ = prefill_inputs(p)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 4, 512), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated(DEV)
+    fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated(DEV) == before
+    o2, none = fa.prefill(q, k, v, causal=True, scale=p.scale, return_lse=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
+def test_rejects_cpu_tensors():
+    p = workloads.make_prefill(22, 1, 8, 8, 1, 1, 64, "f32")
+    t = torch.from_numpy(p.q)
+    with pytest.raises(ValueError):
+        fa.prefill(t, t, t)

@@ -1,0 +1,191 @@
+"""Fused attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/fa.h`` (``libfa.so``).
+PyTorch only supplies device memory and the current HIP stream; every step
+of the computation runs in the library's HIP kernels.  There is no CPU or
+PyTorch fallback: without the built library, or with tensors that are not
+on a GPU, the calls raise.
+
+    o, lse = prefill(q, k, v, causal=True)            # q: [B, Nq, Hq, d]
+    o, lse = decode(q, k_cache, v_cache, seqlens_k)   # q: [B, Hq, d]
+
+Both mirror the pages' fused operators: ``flash_attention(query, key, value,
+causal, softmax_scale)`` (jsqmd.com ops-transformer practice page, sections
+一 and 二) with valid lengths in place of a padding mask (``actual_seq_q`` /
+``actual_seq_kv`` of the agent.csdn.net BERT page, chapter 三), and the
+incremental decode of the BERT page's closing section.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import FAError  # noqa: F401
+
+__all__ = ["prefill", "decode", "decode_workspace_size", "FAError", "load_library"]
+
+
+def load_library():
+    """Load ``libfa.so`` (raises ImportError if it has not been built)."""
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _require_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on a GPU device (no CPU fallback exists)")
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _seqlens(x, B, device):
+    torch = _torch()
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        x = torch.tensor(list(x), dtype=torch.int32)
+    x = x.to(device=device, dtype=torch.int32).contiguous()
+    if x.numel() != B:
+        raise ValueError(f"seqlens must have {B} entries")
+    return x
+
+
+def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[float] = None,
+            seqlens_q=None, seqlens_k=None, out=None, lse=None, return_lse: bool = True
+            ) -> Tuple[object, object]:
+    """Fused attention forward for a batch of sequences.
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (any strides with a unit last
+    stride), bf16 or fp32.  Returns ``(o, lse)`` with o like q ([B, Nq, Hq, d],
+    contiguous) and lse fp32 [B, Hq, Nq] (natural log), or ``(o, None)`` when
+    ``return_lse`` is False.  ``window`` keeps the last ``window`` keys up to
+    and including the diagonal; ``seqlens_q`` / ``seqlens_k`` are per-sequence
+    valid lengths (rows past ``seqlens_q`` come back as O = 0, LSE = -inf).
+    """
+    torch = _torch()
+    _require_gpu(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [batch, seq, heads, head_dim]")
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"incompatible shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have a unit head_dim stride")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Nq, Hq, d), dtype=q.dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    sq = _seqlens(seqlens_q, B, dev)
+    sk = _seqlens(seqlens_k, B, dev)
+    p = _lib.PrefillParams()
+    p.dtype = _dtype_code(q)
+    p.batch, p.seqlen_q, p.seqlen_k = B, Nq, Nk
+    p.heads_q, p.heads_kv, p.head_dim = Hq, Hkv, d
+    p.causal = 1 if causal else 0
+    p.window_left = int(window)
+    p.softmax_scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    p.q, p.k, p.v, p.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()
+    p.lse = lse.data_ptr() if (return_lse and lse is not None) else None
+    p.seqlens_q = sq.data_ptr() if sq is not None else None
+    p.seqlens_k = sk.data_ptr() if sk is not None else None
+    p.q_stride[:] = [q.stride(0), q.stride(1), q.stride(2)]
+    p.k_stride[:] = [k.stride(0), k.stride(1), k.stride(2)]
+    p.v_stride[:] = [v.stride(0), v.stride(1), v.stride(2)]
+    p.o_stride[:] = [out.stride(0), out.stride(1), out.stride(2)]
+    _lib.check(_lib.prefill_fwd(p, _stream(dev)), "fa_prefill_fwd")
+    return out, (lse if return_lse else None)
+
+
+def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys):
+    B, Hq, d = q.shape
+    _, cap, Hkv, _ = k_cache.shape
+    p = _lib.DecodeParams()
+    p.dtype = _dtype_code(q)
+    p.batch, p.heads_q, p.heads_kv, p.head_dim = B, Hq, Hkv, d
+    p.cache_capacity = cap
+    p.window_left = int(window)
+    p.chunk_keys = int(chunk_keys)
+    p.softmax_scale = float(1.0 / math.sqrt(d) if scale is None else scale)
+    p.reserved0 = 0
+    p.q = q.data_ptr()
+    p.k_cache, p.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    p.o = out.data_ptr() if out is not None else None
+    p.lse = lse.data_ptr() if lse is not None else None
+    p.seqlens_k = sk.data_ptr() if sk is not None else None
+    p.q_stride[:] = [q.stride(0), q.stride(1)]
+    p.k_stride[:] = [k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)]
+    p.v_stride[:] = [v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)]
+    if out is not None:
+        p.o_stride[:] = [out.stride(0), out.stride(1)]
+    return p
+
+
+def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
+                          chunk_keys: int = 0) -> int:
+    """Workspace bytes ``decode`` needs for these shapes (host-only)."""
+    p = _decode_params(q, k_cache, v_cache, None, None, None, scale, window, chunk_keys)
+    st, n = _lib.decode_workspace_size(p)
+    _lib.check(st, "fa_decode_workspace_size")
+    return n
+
+
+def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, window: int = -1,
+           chunk_keys: int = 0, workspace=None, out=None, lse=None, return_lse: bool = True):
+    """Single-token decode over a contiguous KV cache.
+
+    q: [B, Hq, d]; k_cache, v_cache: [B, capacity, Hkv, d]; seqlens_k: [B]
+    valid lengths (the current token already appended).  Returns ``(o, lse)``:
+    o [B, Hq, d] like q, lse fp32 [B, Hq].  ``workspace`` (a uint8 GPU tensor
+    of at least ``decode_workspace_size`` bytes) may be passed to avoid an
+    allocation per call.
+    """
+    torch = _torch()
+    _require_gpu(q, k_cache, v_cache)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, Hq, d] and caches [B, capacity, Hkv, d]")
+    B, Hq, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match q")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a unit head_dim stride")
+    dev = q.device
+    sk = _seqlens(seqlens_k, B, dev)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=q.dtype, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    p = _decode_params(q, k_cache, v_cache, sk, out, lse if return_lse else None, scale, window,
+                       chunk_keys)
+    st, need = _lib.decode_workspace_size(p)
+    _lib.check(st, "fa_decode_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(_lib.decode_fwd(p, workspace.data_ptr(), ws_bytes, _stream(dev)), "fa_decode_fwd")
+    return out, (lse if return_lse else None)

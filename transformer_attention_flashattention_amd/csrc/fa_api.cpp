@@ -1,0 +1,238 @@
+// C-ABI entry points of the fused-attention library (declared in fa.h).
+//
+// This layer validates every argument on the host before any HIP call,
+// converts the public parameter structs into kernel arguments, sizes the
+// grids and enqueues the kernels on the caller's stream.  It allocates
+// nothing and keeps no state between calls except a thread-local error text.
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+fa_status ok() {
+    g_last_error.clear();
+    return FA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+fa_status check_scale(float scale) {
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(FA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+    return FA_OK;
+}
+
+fa_status check_strides(const char *name, const int64_t *st, int n, int vec) {
+    for (int i = 0; i < n; ++i) {
+        if (st[i] < 0) return fail(FA_ERR_INVALID_ARG, "%s_stride[%d] is negative", name, i);
+        if (st[i] % vec != 0)
+            return fail(FA_ERR_UNSUPPORTED,
+                        "%s_stride[%d] = %lld is not a multiple of %d elements (16-byte vector access)",
+                        name, i, (long long)st[i], vec);
+    }
+    return FA_OK;
+}
+
+#define FA_TRY(expr)                      \
+    do {                                  \
+        fa_status _s = (expr);            \
+        if (_s != FA_OK) return _s;       \
+    } while (0)
+
+// Decode: query heads per workgroup (a divisor of the GQA group, at most 4).
+int decode_heads_per_wg(int group) {
+    if (group % 4 == 0) return 4;
+    if (group % 2 == 0) return 2;
+    return 1;
+}
+
+int decode_chunk(const fa_decode_params *p, int gt) {
+    if (p->chunk_keys > 0) return p->chunk_keys;
+    // Largest chunk that still leaves enough workgroups to fill 256 CUs
+    // several times over when every sequence is at capacity.
+    const long long groups = (long long)p->batch * p->heads_kv * (p->heads_q / p->heads_kv / gt);
+    int c = 256;
+    while (c > 64 && groups * ((p->cache_capacity + c - 1) / c) < 2048) c >>= 1;
+    return c;
+}
+
+fa_status validate_decode(const fa_decode_params *p) {
+    if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+    if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32)
+        return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    if (p->dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "decode supports bf16 only");
+    if (p->batch < 0) return fail(FA_ERR_INVALID_ARG, "batch must be >= 0");
+    if (p->heads_q <= 0 || p->heads_kv <= 0)
+        return fail(FA_ERR_INVALID_ARG, "heads_q and heads_kv must be >= 1");
+    if (p->heads_q % p->heads_kv != 0)
+        return fail(FA_ERR_INVALID_ARG, "heads_q (%d) must be a multiple of heads_kv (%d)", p->heads_q,
+                    p->heads_kv);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+    if (p->cache_capacity < 1) return fail(FA_ERR_INVALID_ARG, "cache_capacity must be >= 1");
+    if (p->window_left == 0 || p->window_left < -1)
+        return fail(FA_ERR_INVALID_ARG, "window_left must be -1 or >= 1 (got %d)", p->window_left);
+    if (p->chunk_keys != 0 && p->chunk_keys != 64 && p->chunk_keys != 128 && p->chunk_keys != 256)
+        return fail(FA_ERR_UNSUPPORTED, "chunk_keys must be 0, 64, 128 or 256 (got %d)", p->chunk_keys);
+    if (p->reserved0 != 0) return fail(FA_ERR_INVALID_ARG, "reserved0 must be 0");
+    FA_TRY(check_scale(p->softmax_scale));
+    FA_TRY(check_strides("q", p->q_stride, 2, 8));
+    FA_TRY(check_strides("k", p->k_stride, 3, 8));
+    FA_TRY(check_strides("v", p->v_stride, 3, 8));
+    FA_TRY(check_strides("o", p->o_stride, 2, 1));
+    if (p->batch == 0) return FA_OK;
+    if (!p->q || !p->k_cache || !p->v_cache || !p->o || !p->seqlens_k)
+        return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache, o and seqlens_k must be non-NULL");
+    if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache))
+        return fail(FA_ERR_UNSUPPORTED, "q, k_cache and v_cache must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(p->o) & 1u) != 0)
+        return fail(FA_ERR_INVALID_ARG, "o must be 2-byte aligned");
+    return FA_OK;
+}
+
+size_t decode_ws_bytes(const fa_decode_params *p, int chunk) {
+    const size_t max_chunks = (size_t)(p->cache_capacity + chunk - 1) / chunk;
+    const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
+    const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
+    const size_t ml_bytes = rows * 2 * sizeof(float);
+    return o_bytes + ml_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char *fa_status_str(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+const char *fa_last_error_message(void) { return g_last_error.c_str(); }
+
+fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
+    if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+    if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32)
+        return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+        return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_k must be >= 0");
+    if (p->heads_q <= 0 || p->heads_kv <= 0)
+        return fail(FA_ERR_INVALID_ARG, "heads_q and heads_kv must be >= 1");
+    if (p->heads_q % p->heads_kv != 0)
+        return fail(FA_ERR_INVALID_ARG, "heads_q (%d) must be a multiple of heads_kv (%d)", p->heads_q,
+                    p->heads_kv);
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(FA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", p->head_dim);
+    if (p->causal != 0 && p->causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (p->window_left == 0 || p->window_left < -1)
+        return fail(FA_ERR_INVALID_ARG, "window_left must be -1 or >= 1 (got %d)", p->window_left);
+    FA_TRY(check_scale(p->softmax_scale));
+    const int vec = p->dtype == FA_DTYPE_BF16 ? 8 : 4;
+    FA_TRY(check_strides("q", p->q_stride, 3, vec));
+    FA_TRY(check_strides("k", p->k_stride, 3, vec));
+    FA_TRY(check_strides("v", p->v_stride, 3, vec));
+    FA_TRY(check_strides("o", p->o_stride, 3, vec));
+    if (p->batch == 0 || p->seqlen_q == 0) return ok();
+    if (!p->q || !p->o) return fail(FA_ERR_INVALID_ARG, "q and o must be non-NULL");
+    if (p->seqlen_k > 0 && (!p->k || !p->v))
+        return fail(FA_ERR_INVALID_ARG, "k and v must be non-NULL when seqlen_k > 0");
+    if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
+        return fail(FA_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+
+    fa::PrefillArgs a{};
+    a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse;
+    a.seqlens_q = p->seqlens_q; a.seqlens_k = p->seqlens_k;
+    a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+    a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+    a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+    a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
+    a.batch = p->batch; a.seqlen_q = p->seqlen_q; a.seqlen_k = p->seqlen_k;
+    a.heads_q = p->heads_q; a.heads_kv = p->heads_kv; a.group = p->heads_q / p->heads_kv;
+    a.causal = p->causal; a.window_left = p->window_left;
+    a.scale = p->softmax_scale;
+    a.scale_log2 = p->softmax_scale * kLog2e;
+    const int bm = p->dtype == FA_DTYPE_BF16 ? fa::kPrefillBM : fa::kPrefillF32BM;
+    a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
+    if ((int64_t)a.num_q_tiles * a.heads_q * a.batch > 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = p->dtype == FA_DTYPE_BF16 ? fa::launch_prefill_bf16(a, p->head_dim, s)
+                                                   : fa::launch_prefill_f32(a, p->head_dim, s);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+fa_status fa_decode_workspace_size(const fa_decode_params *p, size_t *bytes) {
+    if (!bytes) return fail(FA_ERR_INVALID_ARG, "bytes is NULL");
+    FA_TRY(validate_decode(p));
+    const int gt = decode_heads_per_wg(p->heads_q / p->heads_kv);
+    *bytes = p->batch == 0 ? 0 : decode_ws_bytes(p, decode_chunk(p, gt));
+    return ok();
+}
+
+fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+    FA_TRY(validate_decode(p));
+    if (p->batch == 0) return ok();
+    const int group = p->heads_q / p->heads_kv;
+    const int gt = decode_heads_per_wg(group);
+    const int chunk = decode_chunk(p, gt);
+    const size_t need = decode_ws_bytes(p, chunk);
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    const int max_chunks = (p->cache_capacity + chunk - 1) / chunk;
+    if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL || p->batch > 65535 ||
+        (int64_t)p->heads_kv * (group / gt) > 65535)
+        return fail(FA_ERR_UNSUPPORTED, "grid too large");
+
+    fa::DecodeArgs a{};
+    a.q = p->q; a.k = p->k_cache; a.v = p->v_cache; a.o = p->o; a.lse = p->lse;
+    a.seqlens_k = p->seqlens_k;
+    a.q_sb = p->q_stride[0]; a.q_sh = p->q_stride[1];
+    a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+    a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+    a.o_sb = p->o_stride[0]; a.o_sh = p->o_stride[1];
+    a.batch = p->batch; a.heads_q = p->heads_q; a.heads_kv = p->heads_kv; a.group = group;
+    a.capacity = p->cache_capacity; a.window_left = p->window_left;
+    a.chunk = chunk; a.max_chunks = max_chunks; a.head_groups = group / gt;
+    a.scale_log2 = p->softmax_scale * kLog2e;
+    const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
+    const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+
+    const hipError_t e = fa::launch_decode_bf16(a, p->head_dim, gt, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI layer (fa_api.cpp) and the kernel
+// translation units.  Arguments have already been validated on the host when
+// these launchers run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+// Kernel arguments for prefill (both dtypes).  Extents are the padded tensor
+// extents; per-sequence valid lengths come from the optional device arrays.
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    const int32_t *seqlens_q, *seqlens_k;
+    int64_t q_sb, q_ss, q_sh;      // element strides: batch, seq, head
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t o_sb, o_ss, o_sh;
+    int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, group;  // group = heads_q / heads_kv
+    int32_t causal, window_left;
+    float scale_log2;              // softmax_scale * log2(e)
+    float scale;                   // softmax_scale
+    int32_t num_q_tiles;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    const int32_t *seqlens_k;
+    int64_t q_sb, q_sh;
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t o_sb, o_sh;
+    int32_t batch, heads_q, heads_kv, group, capacity, window_left;
+    int32_t chunk;                 // keys per split
+    int32_t max_chunks;            // ceil(capacity / chunk)
+    int32_t head_groups;           // group / heads_per_wg
+    float scale_log2;
+    float *ws_o;                   // [batch, heads_q, max_chunks, head_dim] fp32
+    float *ws_ml;                  // [batch, heads_q, max_chunks, 2] fp32 (m, l)
+};
+
+// Each launcher enqueues its kernel(s) and returns the launch status.
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_wg,
+                              hipStream_t s);
+
+// Tile sizes the launchers use (also needed by the host for grid sizing).
+constexpr int kPrefillBM = 128;    // query rows per workgroup (bf16 path)
+constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
+
+}  // namespace fa
