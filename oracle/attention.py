@@ -88,7 +88,9 @@ def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     s = scale * (q_rows @ k.T)                       # step 1
     s = np.where(vis, s, NEG_INF)                    # step 2
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
-    empty = ~np.isfinite(m)
+    # a row is empty only when no key is visible (m = -inf); NaN inputs on
+    # visible keys propagate to the output as the definition implies
+    empty = np.isneginf(m)
     m_safe = np.where(empty, 0.0, m)
     p = np.exp(s - m_safe[:, None])                  # step 3 (exp(-inf) = 0)
     l = p.sum(axis=1)

@@ -205,7 +205,11 @@ def test_decode_validation(lib, kw, status, needle):
     assert st == status, (_lib.status_str(st), _lib.last_error())
     assert needle in _lib.last_error()
     st2, _ = _lib.decode_workspace_size(p)
-    assert st2 == status
+    if needle in ("seqlens_k", "aligned"):
+        # sizing the workspace needs shapes only, never the data pointers
+        assert st2 == _lib.FA_OK
+    else:
+        assert st2 == status
 
 
 def test_decode_workspace_rules(lib):

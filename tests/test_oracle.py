@@ -421,3 +421,14 @@ def test_generator_hashes_are_stable():
     assert small.sha256() == stored["prefill_small"]
     dec = workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16")
     assert dec.sha256() == stored["decode_small"]
+
+
+def test_nan_on_visible_key_propagates():
+    """Only a row with no visible key is 'empty'; NaN data must not look empty."""
+    q = np.ones((1, 3, 1, 2))
+    k = np.zeros((1, 3, 1, 2))
+    v = np.ones((1, 3, 1, 2))
+    k[0, 1, 0, 0] = np.nan
+    o, lse = oracle.attention(q, k, v, scale=1.0, causal=True)
+    assert np.all(o[0, 0, 0] == 1.0) and lse[0, 0, 0] == math.log(1.0)
+    assert np.all(np.isnan(o[0, 1:, 0])) and np.all(np.isnan(lse[0, 0, 1:]))

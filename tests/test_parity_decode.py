@@ -56,7 +56,9 @@ def test_window(W):
 
 
 def test_lengths_clamped_to_capacity():
-    dp = workloads.make_decode(54, 3, 4, 2, 128, 300, (1, 300), "bf16")
+    # every cache row valid, so lengths beyond capacity clamp onto real data
+    dp = workloads.make_decode(54, 3, 4, 2, 128, 300, (1, 300), "bf16",
+                               lengths=np.array([300, 300, 300], dtype=np.int32))
     q, kc, vc, sk = decode_inputs(dp)
     big = torch.tensor([5000, -7, 300], dtype=torch.int32, device=DEV)
     o, lse = fa.decode(q, kc, vc, big, scale=dp.scale)

@@ -99,6 +99,11 @@ fa_status validate_decode(const fa_decode_params *p) {
     FA_TRY(check_strides("k", p->k_stride, 3, 8));
     FA_TRY(check_strides("v", p->v_stride, 3, 8));
     FA_TRY(check_strides("o", p->o_stride, 2, 1));
+    return FA_OK;
+}
+
+// Pointer checks, needed to launch but not to size the workspace.
+fa_status validate_decode_pointers(const fa_decode_params *p) {
     if (p->batch == 0) return FA_OK;
     if (!p->q || !p->k_cache || !p->v_cache || !p->o || !p->seqlens_k)
         return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache, o and seqlens_k must be non-NULL");
@@ -200,6 +205,7 @@ fa_status fa_decode_workspace_size(const fa_decode_params *p, size_t *bytes) {
 fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t workspace_bytes,
                         void *hip_stream) {
     FA_TRY(validate_decode(p));
+    FA_TRY(validate_decode_pointers(p));
     if (p->batch == 0) return ok();
     const int group = p->heads_q / p->heads_kv;
     const int gt = decode_heads_per_wg(group);
