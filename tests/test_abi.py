@@ -234,3 +234,12 @@ def test_decode_workspace_rules(lib):
     p0 = _decode(batch=0)
     assert _lib.decode_workspace_size(p0) == (_lib.FA_OK, 0)
     assert _lib.decode_fwd(p0, None, 0, 0) == _lib.FA_OK
+
+
+def test_no_unresolved_internal_symbols(lib):
+    """Every kernel launcher links: a kernel whose host-side instantiation fails
+    leaves an undefined device stub behind, which only shows at load time."""
+    out = subprocess.run(["nm", "-D", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    undefined = [l.split()[-1] for l in out.splitlines() if l.strip().startswith("U ")]
+    assert not [s for s in undefined if s.startswith("_ZN2fa")], undefined
