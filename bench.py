@@ -53,6 +53,8 @@ def parse():
                     help="skip the CPU oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-heads", type=int, default=4,
                     help="heads of the prefill workload the CPU oracle times")
+    ap.add_argument("--decode-chunk", type=int, default=0,
+                    help="keys per decode split (0 = library choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -136,7 +138,8 @@ def main():
     sk = torch.from_numpy(dp.seqlens_k).to(dev)
     od = torch.empty_like(qd)
     lsed = torch.empty((Bd, Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(fa.decode_workspace_size(qd, kc, vc), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fa.decode_workspace_size(qd, kc, vc, chunk_keys=args.decode_chunk),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -145,7 +148,8 @@ def main():
         fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        fa.decode(qd, kc, vc, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws)
+        fa.decode(qd, kc, vc, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws,
+                  chunk_keys=args.decode_chunk)
         if ev is not None:
             ev[2].record()
 

@@ -216,8 +216,8 @@ def test_decode_workspace_rules(lib):
     p = _decode()
     st, n = _lib.decode_workspace_size(p)
     assert st == _lib.FA_OK
-    # library choice at this size is 256-key chunks: 32 chunks of 64*32 rows
-    rows = 64 * 32 * 32
+    # library choice at this size is 128-key chunks: 64 chunks of 64*32 rows
+    rows = 64 * 32 * 64
     expect = ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
     assert n == expect
     assert _lib.decode_fwd(p, None, n, 0) == _lib.FA_ERR_WORKSPACE

@@ -236,48 +236,97 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// One workgroup of 4 wavefronts per (sequence, query head).  Every lane of
+// every wavefront holds the (m, l) of one chunk (64 chunks per pass), so each
+// wavefront derives the global max and all weights on its own; wavefront w
+// then sums chunks w, w+4, w+8, ... with all of its partial-O loads issued
+// before the first use, and the four partial sums meet in LDS.  Each
+// (sequence, head) therefore costs about one memory round trip per 64 chunks.
+constexpr int COMBINE_THREADS = 256;
+constexpr int COMBINE_UNROLL = 16;   // chunks per wavefront per pass (64 / 4)
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int DPL = (D + 63) / 64;       // dims per lane
+    __shared__ float part[COMBINE_THREADS / 64][D];
+    __shared__ float lpart[COMBINE_THREADS / 64];
+
     const int bh = blockIdx.x;
     const int b = bh / a.heads_q, h = bh - (bh / a.heads_q) * a.heads_q;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int lo, L;
     visible_range(a, b, lo, L);
     const int C = a.chunk;
     const int c_lo = lo / C, c_hi = (L > lo) ? (L + C - 1) / C : c_lo;
-    const int64_t base = ((int64_t)b * a.heads_q + h) * a.max_chunks;
+    const int n = c_hi - c_lo;
+    const int64_t base = ((int64_t)b * a.heads_q + h) * a.max_chunks + c_lo;
 
     float M = -INFINITY;
-    for (int c = c_lo; c < c_hi; ++c) M = fmaxf(M, a.ws_ml[(base + c) * 2]);
+    for (int j = lane; j < n; j += 64) M = fmaxf(M, a.ws_ml[(base + j) * 2]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float M_use = (M == -INFINITY) ? 0.f : M;
-    float Lsum = 0.f;
-    constexpr int DPL = (D + 63) / 64;       // dims per lane
+
     float acc[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-    for (int c = c_lo; c < c_hi; ++c) {
-        const float w = __builtin_amdgcn_exp2f(a.ws_ml[(base + c) * 2] - M_use);
-        Lsum = __builtin_fmaf(w, a.ws_ml[(base + c) * 2 + 1], Lsum);
-        const float *op = a.ws_o + (base + c) * D;
+    float Lsum = 0.f;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        // partial O rows of this wavefront's chunks in this pass: loads first
+        float ov[COMBINE_UNROLL][DPL];
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-            const int d = lane * DPL + i;
-            if (d < D) acc[i] = __builtin_fmaf(w, op[d], acc[i]);
+        for (int u = 0; u < COMBINE_UNROLL; ++u) {
+            const int j = j0 + wave + 4 * u;
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) {
+                const int d = lane * DPL + i;
+                ov[u][i] = (j < n && d < D) ? a.ws_o[(base + j) * D + d] : 0.f;
+            }
+        }
+        const int jl = j0 + lane;
+        float w = 0.f, lw = 0.f;
+        if (jl < n) {
+            w = __builtin_amdgcn_exp2f(a.ws_ml[(base + jl) * 2] - M_use);
+            lw = w * a.ws_ml[(base + jl) * 2 + 1];
+        }
+        Lsum += lw;
+#pragma unroll
+        for (int u = 0; u < COMBINE_UNROLL; ++u) {
+            const float wc = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), wave + 4 * u));
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(wc, ov[u][i], acc[i]);
         }
     }
-    const bool ok = Lsum > 0.f;
-    const float inv = ok ? 1.f / Lsum : 0.f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+        const int d = lane * DPL + i;
+        if (d < D) part[wave][d] = acc[i];
+    }
+    if (lane == 0) lpart[wave] = Lsum;
+    __syncthreads();
+    if (wave != 0) return;
+
+    // every wavefront summed all chunk weights, so any lpart entry is the total
+    const float Ltot = lpart[0];
+    const bool ok = Ltot > 0.f;
+    const float inv = ok ? 1.f / Ltot : 0.f;
     unsigned short *orow = (unsigned short *)a.o + b * a.o_sb + h * a.o_sh;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
         const int d = lane * DPL + i;
         if (d < D) {
-            const __bf16 x = (__bf16)(acc[i] * inv);
+            float v = part[0][d];
+#pragma unroll
+            for (int w2 = 1; w2 < COMBINE_THREADS / 64; ++w2) v += part[w2][d];
+            const __bf16 x = (__bf16)(v * inv);
             orow[d] = __builtin_bit_cast(unsigned short, x);
         }
     }
     if (a.lse && lane == 0)
-        a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Lsum)) * LN2 : -INFINITY;
+        a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Ltot)) * LN2 : -INFINITY;
 }
 
 template <int D, int GT>
@@ -300,7 +349,8 @@ hipError_t launch_all(const DecodeArgs &a, int gt, hipStream_t s) {
         default: e = launch_split<D, 4>(a, s); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.batch * a.heads_q), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.batch * a.heads_q), dim3(COMBINE_THREADS), 0,
+                       s, a);
     return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_w
                               hipStream_t s);
 
 // Tile sizes the launchers use (also needed by the host for grid sizing).
-constexpr int kPrefillBM = 128;    // query rows per workgroup (bf16 path)
+constexpr int kPrefillBM = 256;    // query rows per workgroup (bf16 path)
 constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
 
 }  // namespace fa

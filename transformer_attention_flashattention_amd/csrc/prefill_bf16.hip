@@ -13,7 +13,8 @@
 // exp, block-local maxima corrected to one common maximum, fp32 for max,
 // exp and normalisation while the matrix products run in 16-bit).
 //
-// Work decomposition (one workgroup = 4 wavefronts = 128 query rows):
+// Work decomposition: one workgroup = 8 wavefronts = 256 query rows of one
+// (batch, head), 32 rows per wavefront.
 //   * grid = query tiles x heads x batch; heads and batches are independent
 //     work items spread over all CUs (jsqmd.com page, section 二 "multi-head
 //     parallel strategy").  Consecutive workgroup ids differ in (batch, head)
@@ -21,15 +22,27 @@
 //     K/V inside one XCD's L2; under a causal mask the longest query tiles are
 //     dispatched first.
 //   * KV tiles of 64 keys move HBM -> LDS with direct-to-LDS loads
-//     (global_load_lds_dwordx4: no VGPR staging), double buffered: tile t+1
-//     streams into one LDS buffer while tile t is computed from the other (the
-//     two-region ping-pong of the hwcomputing.csdn.net page, section 2.1).
+//     (global_load_lds_dwordx4: no VGPR staging) into two K and two V buffers
+//     shared by all 8 wavefronts: the next tiles stream in while the current
+//     ones are read (the two-region ping-pong of the hwcomputing.csdn.net
+//     page, section 2.1).
 //   * the causal / window / valid-length masks are index arithmetic: tiles
-//     wholly outside the visible band are never visited, and the element mask
-//     runs only on tiles that cross a boundary (jsqmd.com page, section 二
-//     "causal mask and decode").  Rows at or beyond the valid key length are
-//     never read: their loads are redirected to the last valid row and the
-//     corresponding scores are masked (agent.csdn.net BERT page, chapter 四).
+//     wholly outside a wavefront's visible band are skipped by that
+//     wavefront, and the element mask runs only on tiles that cross a
+//     boundary (jsqmd.com page, section 二 "causal mask and decode").  Rows
+//     at or beyond the valid key length are never read: their loads are
+//     redirected to the last valid row and their scores masked
+//     (agent.csdn.net BERT page, chapter 四).
+//
+// Matrix/vector overlap (the page's Cube/Vector pipelining, jsqmd.com
+// section 二, done the gfx950 way): the 8 wavefronts form two groups of 4,
+// one wavefront of each group per SIMD.  Time is cut into phases separated
+// by workgroup barriers; in every phase one group runs its matrix step
+// (PV of the previous tile, then S = K Q^T of the current tile: 32 MFMAs)
+// while the other group runs its softmax step on the VALU (max, exp, P in
+// bf16, row sums, rare O rescale).  Group B lags group A by one phase, so
+// each SIMD always has one wavefront feeding the matrix core and one feeding
+// the vector ALU.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, 64 lanes):
 //   S^T[key][query] = K Q^T : A = K rows from LDS, B = Q held in registers.
@@ -51,6 +64,8 @@
 // exceeds it by more than 2^8 (in the base-2 exponent domain); until then P
 // is taken against the old reference, so O, the row sum and P always share
 // one reference and the result is exact -- only the rescale work is skipped.
+// The row sum adds the fp32 P values (before their bf16 rounding for the PV
+// product), so LSE carries only fp32 rounding.
 #include "fa_internal.h"
 
 #include <climits>
@@ -60,16 +75,23 @@ namespace fa {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
 
 constexpr int BM = kPrefillBM;   // query rows per workgroup
 constexpr int BN = 64;           // keys per KV tile
-constexpr int NTHREADS = 256;
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = NWAVES * 64;
+static_assert(BM == NWAVES * 32, "one 32-row block per wavefront");
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the largest un-rescaled p
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DS_READ = 0x100;
 
 // Row permutation of a 32-key sub-block: swap bits 2 and 3.
 __device__ __forceinline__ int perm32(int m) {
@@ -82,16 +104,15 @@ struct Tile {
     static constexpr int CH = D / 8;             // 16-byte chunks per row
     static constexpr int RPW = 256 / ROWB;       // rows per 256-byte LDS bank window
     static constexpr int BYTES = BN * ROWB;      // bytes per K or V tile
-    static constexpr int LOADS_PER_WAVE = BYTES / 1024 / 4;
+    static constexpr int LOADS_PER_WAVE = BYTES / 1024 / NWAVES;
     // physical chunk of logical chunk c in row r
-    __device__ static __forceinline__ int k_chunk(int r, int c) { return c ^ ((r / RPW) & (CH - 1)); }
-    __device__ static __forceinline__ int v_chunk(int r, int c) {
+    __host__ __device__ static constexpr int k_chunk(int r, int c) { return c ^ ((r / RPW) & (CH - 1)); }
+    __host__ __device__ static constexpr int v_chunk(int r, int c) {
         return c ^ ((((r / RPW) & 3) << 2) & (CH - 1));
     }
 };
 
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     bf16x2 r;
     r[0] = (__bf16)lo;
     r[1] = (__bf16)hi;
@@ -103,6 +124,11 @@ __device__ __forceinline__ void wait_loads() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+__device__ __forceinline__ void lds_dma16(const char *g, char *l) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
@@ -112,13 +138,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
     constexpr int DBLK = D / 32;          // 32-dim row blocks of O^T
 
     __shared__ __attribute__((aligned(1024))) char sK0[T::BYTES];
-    __shared__ __attribute__((aligned(1024))) char sV0[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char sK1[T::BYTES];
+    __shared__ __attribute__((aligned(1024))) char sV0[T::BYTES];
     __shared__ __attribute__((aligned(1024))) char sV1[T::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int grp = wave >> 2;            // 0: leading group, 1: lagging group
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
@@ -138,22 +165,35 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int offset = Lk - Lq;           // bottom-right causal alignment
     const int W = a.window_left;
 
-    int kv_lo = 0, kv_hi = Lk;
-    if (q0 < Lq) {
-        const int q_last = min(q0 + BM, Lq) - 1;
-        if (a.causal) kv_hi = min(kv_hi, q_last + offset + 1);
-        if (W > 0) kv_lo = max(0, q0 + offset - W + 1);
+    // visible key range [lo, hi) of a block of rows [r0, r1] (all < Lq)
+    auto key_range = [&](int r0, int r1, int &lo, int &hi) {
+        lo = 0;
+        hi = Lk;
+        if (a.causal) hi = min(hi, r1 + offset + 1);
+        if (W > 0) lo = max(0, r0 + offset - W + 1);
+    };
+    int wg_lo = 0, wg_hi = 0;
+    if (q0 < Lq) key_range(q0, min(q0 + BM, Lq) - 1, wg_lo, wg_hi);
+    const int t_begin = wg_lo / BN;
+    const int ntiles = (wg_hi > wg_lo) ? (wg_hi + BN - 1) / BN - t_begin : 0;
+
+    const int q0w = q0 + wave * 32;       // first query row of this wavefront
+    const int qi = q0w + l32;             // this lane's query row
+    // tiles (relative to t_begin) this wavefront has to visit: [w_lo, w_hi)
+    int w_lo = 0, w_hi = 0;
+    if (q0w < Lq && ntiles > 0) {
+        int lo, hi;
+        key_range(q0w, min(q0w + 32, Lq) - 1, lo, hi);
+        if (hi > lo) {
+            w_lo = lo / BN - t_begin;
+            w_hi = (hi + BN - 1) / BN - t_begin;
+        }
     }
-    const int t_begin = kv_lo / BN;
-    int t_end = (kv_hi + BN - 1) / BN;
-    if (q0 >= Lq || kv_hi <= kv_lo) t_end = t_begin;   // nothing visible
 
     const unsigned short *Qp = (const unsigned short *)a.q + b * a.q_sb + h * a.q_sh;
-    const unsigned short *Kp = (const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh;
-    const unsigned short *Vp = (const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh;
-
-    const int q0w = q0 + wave * 32;       // first query row of this wave
-    const int qi = q0w + l32;             // this lane's query row
+    const char *Kp = (const char *)((const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh);
+    const char *Vp = (const char *)((const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh);
+    const int64_t k_row_bytes = a.k_ss * 2, v_row_bytes = a.v_ss * 2;
 
     // ---- Q fragment (B operand), zero for rows outside the valid length ---
     bf16x8 qf[KSTEPS];
@@ -168,25 +208,60 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
     }
 
-    // ---- HBM -> LDS, one KV tile, 1 KiB per wavefront instruction ----------
-    auto issue_tile = [&](int t, char *kb, char *vb) {
-        const int k0 = t * BN;
+    // ---- HBM -> LDS: each wavefront writes LOADS_PER_WAVE x 1 KiB per tile --
+    // For load i the lane's tile row and physical chunk are fixed; only the
+    // tile base moves, so full tiles use a uniform base plus a per-lane offset.
+    int ld_row[T::LOADS_PER_WAVE];
+    unsigned k_loff[T::LOADS_PER_WAVE], v_loff[T::LOADS_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
-            const int ins = wave * T::LOADS_PER_WAVE + i;
-            const int lin = ins * 1024 + lane * 16;
-            const int r = lin / T::ROWB;
-            const int p = (lin % T::ROWB) >> 4;
-            const int row = min(k0 + r, Lk - 1);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(Kp + (int64_t)row * a.k_ss + T::k_chunk(r, p) * 8),
-                (__attribute__((address_space(3))) void *)(kb + ins * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(Vp + (int64_t)row * a.v_ss + T::v_chunk(r, p) * 8),
-                (__attribute__((address_space(3))) void *)(vb + ins * 1024), 16, 0, 0);
+    for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+        const int lin = (wave * T::LOADS_PER_WAVE + i) * 1024 + lane * 16;
+        const int r = lin / T::ROWB;
+        const int p = (lin % T::ROWB) >> 4;
+        ld_row[i] = r;
+        k_loff[i] = (unsigned)(r * k_row_bytes) + (unsigned)(T::k_chunk(r, p) << 4);
+        v_loff[i] = (unsigned)(r * v_row_bytes) + (unsigned)(T::v_chunk(r, p) << 4);
+    }
+    auto issue = [&](const char *base, int64_t row_bytes, const unsigned *loff, int t, char *buf,
+                     bool is_k) {
+        const int k0 = (t_begin + t) * BN;
+        const char *tb = base + (int64_t)k0 * row_bytes;
+        if (k0 + BN <= Lk) {
+#pragma unroll
+            for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
+                lds_dma16(tb + loff[i], buf + (wave * T::LOADS_PER_WAVE + i) * 1024);
+        } else {
+            // last tile: rows past the valid length re-read the last valid row
+#pragma unroll
+            for (int i = 0; i < T::LOADS_PER_WAVE; ++i) {
+                const int r = ld_row[i];
+                const int lin = (wave * T::LOADS_PER_WAVE + i) * 1024 + lane * 16;
+                const int p = (lin % T::ROWB) >> 4;
+                const int row = min(k0 + r, Lk - 1);
+                const int c = is_k ? T::k_chunk(r, p) : T::v_chunk(r, p);
+                lds_dma16(base + (int64_t)row * row_bytes + (c << 4),
+                          buf + (wave * T::LOADS_PER_WAVE + i) * 1024);
+            }
         }
     };
+    auto issue_k = [&](int t, char *buf) { issue(Kp, k_row_bytes, k_loff, t, buf, true); };
+    auto issue_v = [&](int t, char *buf) { issue(Vp, v_row_bytes, v_loff, t, buf, false); };
 
+    // ---- per-lane LDS operand offsets (loop invariant) ----------------------
+    const int kr = perm32(l32);                      // K row within a 32-key sub-block
+    int k_off[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) k_off[ks] = kr * T::ROWB + (T::k_chunk(kr, ks * 2 + half) << 4);
+    const int g16 = lane >> 4, r16 = lane & 15;
+    const int v_row_lane = 8 * half + (r16 >> 2);    // + 16 * ksp + 4 * tt
+    int v_off[DBLK];
+#pragma unroll
+    for (int jd = 0; jd < DBLK; ++jd) {
+        const int c = 4 * jd + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+        v_off[jd] = v_row_lane * T::ROWB + (T::v_chunk(v_row_lane, c) << 4) + (r16 & 1) * 8;
+    }
+
+    // ---- per-lane softmax state ----------------------------------------------
     f32x16 oacc[DBLK];
 #pragma unroll
     for (int jd = 0; jd < DBLK; ++jd)
@@ -194,43 +269,86 @@ void prefill_bf16_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) oacc[jd][r] = 0.f;
     float m_ref = -INFINITY;   // reference row max, scaled log2 domain
     float l_run = 0.f;         // running row sum over this lane's keys
+    f32x16 s[2];               // S^T of the tile in flight (matrix -> softmax step)
+    bf16x8 pb[4];              // P^T of the tile in flight (softmax -> matrix step)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-    const int pos = qi + offset;                       // key position of this row
+    const int pos = qi + offset;                     // key position of this row
     const float c2 = a.scale_log2;
     const int vis_hi = a.causal ? min(Lk, pos + 1) : Lk;
     const int vis_lo = (W > 0) ? pos - W + 1 : INT_MIN;
 
-    // per-lane constant parts of the LDS operand addresses
-    int k_row[2];
+    // matrix step of tile j: PV of tile j-1 (from vb), then S of tile j (from kb).
+    // Operand reads are issued in the order the MFMAs consume them and the
+    // schedule keeps the reads a few MFMAs ahead, so LDS latency hides under
+    // matrix work instead of stalling every MFMA; consecutive MFMAs use
+    // different accumulators.
+    auto matrix_step = [&](int j, const char *kb, const char *vb) {
+        if (j - 1 >= w_lo && j - 1 < w_hi) {
+            bf16x8 vf[4][DBLK];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) k_row[sb] = sb * 32 + perm32(l32);
-    const int g16 = lane >> 4, r16 = lane & 15;
-
-    auto compute_tile = [&](int t, const char *kb, const char *vb) {
-        const int k0 = t * BN;
-
-        // S^T = K Q^T for two 32-key sub-blocks: all K fragments are read
-        // first, then the two independent accumulation chains alternate.
-        f32x16 s[2];
-        bf16x8 kf[2][KSTEPS];
+            for (int ksp = 0; ksp < 4; ++ksp)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int r = k_row[sb];
-            const char *krow = kb + r * T::ROWB;
+                for (int jd = 0; jd < DBLK; ++jd) {
+                    s16x4 part[2];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)(vb + v_off[jd] +
+                                                                        (16 * ksp + 4 * tt) * T::ROWB));
+                    vf[ksp][jd] = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+#pragma unroll
+            for (int ksp = 0; ksp < 4; ++ksp)
+#pragma unroll
+                for (int jd = 0; jd < DBLK; ++jd)
+                    oacc[jd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksp][jd], pb[ksp], oacc[jd], 0, 0, 0);
+            // 2 DS reads per MFMA, kept 4 MFMAs ahead
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+#pragma unroll
+            for (int i = 0; i < 4 * DBLK - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+        }
+        if (j >= w_lo && j < w_hi) {
+            bf16x8 kf[KSTEPS][2];
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
-                kf[sb][ks] = *(const bf16x8 *)(krow + (T::k_chunk(r, ks * 2 + half) << 4));
 #pragma unroll
-            for (int r2 = 0; r2 < 16; ++r2) s[sb][r2] = 0.f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
+                for (int sb = 0; sb < 2; ++sb)
+                    kf[ks][sb] = *(const bf16x8 *)(kb + sb * 32 * T::ROWB + k_off[ks]);
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
-                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sb][ks], qf[ks], s[sb], 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+                    s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][sb], qf[ks], s[sb], 0, 0, 0);
+            // 1 DS read per MFMA, kept 4 MFMAs ahead
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KSTEPS - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+        }
+    };
 
-        // element mask (branch-free), only on tiles that cross a boundary of
-        // this wave's rows: visible keys of this row are [vis_lo, vis_hi)
+    // softmax step of tile j: mask, running max, P in bf16, row sums
+    auto softmax_step = [&](int j) {
+        if (!(j >= w_lo && j < w_hi)) return;
+        const int k0 = (t_begin + j) * BN;
         const bool need_mask = (k0 + BN > Lk) ||
                                (a.causal && k0 + BN - 1 > q0w + offset) ||
                                (W > 0 && k0 <= q0w + 31 + offset - W);
@@ -243,8 +361,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
                     s[sb][r] = (key >= vis_lo && key < vis_hi) ? s[sb][r] : -INFINITY;
                 }
         }
-
-        // online softmax (fp32, base-2 exponent with the scale folded in)
         float mx = s[0][0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
@@ -253,7 +369,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_ref, mx * c2);
         if (__ballot(m_new > m_ref + RESCALE_THRESHOLD)) {
-            // move the reference: at least one row of this wave grew too far
+            // move the reference: at least one row of this wavefront grew too far
             const float m_to = (m_new > m_ref + RESCALE_THRESHOLD) ? m_new : m_ref;
             // 1 for rows that keep their reference (also when both are -inf),
             // 0 when the old reference is -inf (nothing accumulated yet)
@@ -266,69 +382,59 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) oacc[jd][r] *= alpha;
         }
         const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-        bf16x8 pb[4];
         float psum = 0.f;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c2, -m_use));
-                psum += p[r];
-            }
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 u32x4 w;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[tt * 8 + 2 * i], p[tt * 8 + 2 * i + 1]);
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i], c2, -m_use));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i + 1], c2, -m_use));
+                    w[i] = pack_bf16x2(p0, p1);
+                    psum += p0 + p1;
+                }
                 pb[sb * 2 + tt] = __builtin_bit_cast(bf16x8, w);
             }
-        }
         l_run += psum;
-
-        // O^T += V^T P^T ; V^T operand from the row-major V tile by transpose
-        // reads, all four key steps of a 32-dim block fetched before its MFMAs
-#pragma unroll
-        for (int jd = 0; jd < DBLK; ++jd) {
-            const int c = 4 * jd + 2 * (g16 & 1) + ((r16 & 3) >> 1);
-            const int byte_in_chunk = (r16 & 1) * 8;
-            bf16x8 vf[4];
-#pragma unroll
-            for (int ksp = 0; ksp < 4; ++ksp) {
-                s16x4 part[2];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const int row = 16 * ksp + 8 * half + 4 * tt + (r16 >> 2);
-                    const char *addr = vb + row * T::ROWB + (T::v_chunk(row, c) << 4) + byte_in_chunk;
-                    part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(addr));
-                }
-                typedef __attribute__((ext_vector_type(8))) short s16x8;
-                const s16x8 both = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                vf[ksp] = __builtin_bit_cast(bf16x8, both);
-            }
-#pragma unroll
-            for (int ksp = 0; ksp < 4; ++ksp)
-                oacc[jd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksp], pb[ksp], oacc[jd], 0, 0, 0);
-        }
     };
 
-    // ---- main loop: two statically named LDS buffers, unrolled by two -------
-    if (t_begin < t_end) issue_tile(t_begin, sK0, sV0);
+    // ---- phase loop ----------------------------------------------------------
+    // Phase p: the leading group runs step p, the lagging group step p - 1;
+    // step 2j is the matrix step of tile j, step 2j+1 its softmax step.  At
+    // even phase 2j every wavefront issues K of tile j+1 and V of tile j; they
+    // must land by the end of phase 2j+1.  Unrolled by four phases so every
+    // LDS buffer is named statically.
+    const int nph = ntiles > 0 ? 2 * ntiles + 2 : 0;
+    if (ntiles > 0) issue_k(0, sK0);
     wait_loads();
     __syncthreads();
-    for (int t = t_begin; t < t_end; t += 2) {
-        if (t + 1 < t_end) issue_tile(t + 1, sK1, sV1);
-        compute_tile(t, sK0, sV0);
+    for (int p = 0; p < nph; p += 4) {
+        const int j = p >> 1;             // even tile index of this unrolled block
+        // phase p (= 2j): leading: matrix(j) ; lagging: softmax(j-1)
+        if (j + 1 < ntiles) issue_k(j + 1, sK1);
+        if (j < ntiles) issue_v(j, sV0);
+        if (grp == 0) matrix_step(j, sK0, sV1);
+        else softmax_step(j - 1);
+        __syncthreads();
+        // phase p+1: leading: softmax(j) ; lagging: matrix(j)
+        if (grp == 0) softmax_step(j);
+        else matrix_step(j, sK0, sV1);
         wait_loads();
         __syncthreads();
-        if (t + 1 < t_end) {
-            if (t + 2 < t_end) issue_tile(t + 2, sK0, sV0);
-            compute_tile(t + 1, sK1, sV1);
-            wait_loads();
-            __syncthreads();
-        }
+        if (p + 2 >= nph) break;
+        // phase p+2 (= 2(j+1)): leading: matrix(j+1) ; lagging: softmax(j)
+        if (j + 2 < ntiles) issue_k(j + 2, sK0);
+        if (j + 1 < ntiles) issue_v(j + 1, sV1);
+        if (grp == 0) matrix_step(j + 1, sK1, sV0);
+        else softmax_step(j);
+        __syncthreads();
+        // phase p+3: leading: softmax(j+1) ; lagging: matrix(j+1)
+        if (grp == 0) softmax_step(j + 1);
+        else matrix_step(j + 1, sK1, sV0);
+        wait_loads();
+        __syncthreads();
     }
 
     // ---- epilogue: normalise once, write O (bf16, RNE) and LSE -------------
