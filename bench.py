@@ -44,6 +44,30 @@ def decode_bytes(seqlens, Hq, Hkv, d, elt=2):
     return kv + q_o + len(seqlens) * Hq * 4 + len(seqlens) * 4
 
 
+def measured_traffic(kernels):
+    """HBM bytes per launch of the named kernels, from the committed counter
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a copy-kernel calibration), or
+    None when any of their sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)["kernels"]
+        total = 0
+        for name in kernels:
+            ent = data[name]
+            h = hashlib.sha256()
+            for src in ent["sources"]:
+                with open(os.path.join(ROOT, src), "rb") as f:
+                    h.update(f.read())
+            if h.hexdigest() != ent["sources_sha256"]:
+                return None
+            total += ent["traffic_bytes"]
+        return total
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,10 +229,11 @@ def main():
                    "algorithmic_bytes": dbytes},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(["prefill_bf16_kernel<128>"])},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "traffic": None},
+                            "traffic": measured_traffic(["decode_split_kernel",
+                                                         "decode_combine_kernel<128>"])},
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:

@@ -92,7 +92,10 @@ typedef enum {
  * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
  * window_left == -1 or >= 1; extents >= 0; seqlens arrays (if given) are
  * device int32 [batch].  Pointers must be 16-byte aligned and strides of
- * batch/seq/head multiples of 8 elements (bf16) or 4 elements (fp32).
+ * batch/seq/head multiples of 8 elements (bf16) or 4 elements (fp32); for
+ * bf16 the seq strides of k and v must be below 2^25 elements.  A request
+ * outside these limits returns FA_ERR_UNSUPPORTED or FA_ERR_INVALID_ARG
+ * without launching anything.
  */
 typedef struct {
     int32_t dtype;                       /* fa_dtype; q, k, v and o share it     */

@@ -139,6 +139,8 @@ def _prefill(**kw):
     (dict(q=None), _lib.FA_ERR_INVALID_ARG, "non-NULL"),
     (dict(v=None), _lib.FA_ERR_INVALID_ARG, "non-NULL"),
     (dict(o=FAKE + 2), _lib.FA_ERR_UNSUPPORTED, "aligned"),
+    (dict(k_stride=[1 << 30, 1 << 25, 128]), _lib.FA_ERR_UNSUPPORTED, "2^25"),
+    (dict(v_stride=[1 << 30, 1 << 25, 128]), _lib.FA_ERR_UNSUPPORTED, "2^25"),
 ])
 def test_prefill_validation(lib, kw, status, needle):
     p = _prefill(**kw)

@@ -165,6 +165,9 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     FA_TRY(check_strides("k", p->k_stride, 3, vec));
     FA_TRY(check_strides("v", p->v_stride, 3, vec));
     FA_TRY(check_strides("o", p->o_stride, 3, vec));
+    // the bf16 kernel addresses the rows of one 64-key tile with 32-bit byte offsets
+    if (p->dtype == FA_DTYPE_BF16 && (p->k_stride[1] >= (1LL << 25) || p->v_stride[1] >= (1LL << 25)))
+        return fail(FA_ERR_UNSUPPORTED, "k_stride[1] and v_stride[1] must be below 2^25 elements for bf16");
     if (p->batch == 0 || p->seqlen_q == 0) return ok();
     if (!p->q || !p->o) return fail(FA_ERR_INVALID_ARG, "q and o must be non-NULL");
     if (p->seqlen_k > 0 && (!p->k || !p->v))

@@ -124,9 +124,33 @@ __device__ __forceinline__ void wait_loads() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Combine a value with the one held by the partner lane (lane ^ 32) using
+// v_permlane32_swap, a VALU lane swap, instead of a ds_bpermute shuffle that
+// would queue in the LDS pipe behind the matrix wavefront's operand reads.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// One direct-to-LDS load: each lane moves 16 bytes from its global address g
+// to LDS address l0 + 16 * lane, l0 being the wavefront-uniform LDS address l
+// of lane 0 (passed in M0, which needs one wait state before the load reads
+// it).  Issued as inline assembly so that the compiler's wait-count pass does
+// not see an in-flight load that also writes LDS: it would then drain every
+// LDS read of the loop to zero (lgkmcnt(0)) while the load is outstanding.
+// Completion is tracked explicitly with wait_loads() and the barrier after it.
 __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
-                                     (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+    const unsigned la = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)l;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(la))
+                 : "memory", "m0");
 }
 
 template <int D>
@@ -366,7 +390,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = pair_max(mx);
         const float m_new = fmaxf(m_ref, mx * c2);
         if (__ballot(m_new > m_ref + RESCALE_THRESHOLD)) {
             // move the reference: at least one row of this wavefront grew too far
@@ -438,7 +462,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
 
     // ---- epilogue: normalise once, write O (bf16, RNE) and LSE -------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(l_run);
     const bool row_ok = qi < Lq && l_tot > 0.f;
     const float inv = row_ok ? 1.f / l_tot : 0.f;
     if (qi < a.seqlen_q) {
