@@ -140,8 +140,9 @@ typedef struct {
  * K/V row once for all heads_q / heads_kv query heads of its group, and merge
  * the per-chunk partial results with a log-sum-exp combine pass.
  *
- * chunk_keys: 0 lets the library choose; otherwise 64, 128 or 256.  Results
- * agree to rounding for every choice.
+ * chunk_keys: 0 lets the library choose; otherwise a multiple of 128 keys,
+ * at most 65536 (other values return FA_ERR_UNSUPPORTED).  Results agree to
+ * rounding for every choice.
  *
  * Workspace: fa_decode_workspace_size() reports the bytes fa_decode_fwd needs
  * for this parameter set (it depends on batch, heads, head_dim, capacity and
@@ -161,7 +162,7 @@ typedef struct {
     int32_t head_dim;
     int32_t cache_capacity;              /* rows allocated per sequence          */
     int32_t window_left;                 /* -1 = none, else W >= 1               */
-    int32_t chunk_keys;                  /* 0 = library choice, or 64/128/256    */
+    int32_t chunk_keys;                  /* 0 = library choice, or k * 128       */
     float softmax_scale;
     int32_t reserved0;                   /* must be 0                            */
     const void *q;

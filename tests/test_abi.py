@@ -195,6 +195,9 @@ def _decode(**kw):
     (dict(cache_capacity=0), _lib.FA_ERR_INVALID_ARG, "capacity"),
     (dict(window_left=0), _lib.FA_ERR_INVALID_ARG, "window"),
     (dict(chunk_keys=100), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
+    (dict(chunk_keys=64), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
+    (dict(chunk_keys=-128), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
+    (dict(chunk_keys=65536 + 128), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
     (dict(reserved0=1), _lib.FA_ERR_INVALID_ARG, "reserved0"),
     (dict(softmax_scale=float("inf")), _lib.FA_ERR_INVALID_ARG, "softmax_scale"),
     (dict(seqlens_k=None), _lib.FA_ERR_INVALID_ARG, "seqlens_k"),
@@ -218,8 +221,8 @@ def test_decode_workspace_rules(lib):
     p = _decode()
     st, n = _lib.decode_workspace_size(p)
     assert st == _lib.FA_OK
-    # library choice at this size is 128-key chunks: 64 chunks of 64*32 rows
-    rows = 64 * 32 * 64
+    # library choice at this size is 1024-key chunks: 8 chunks of 64*32 rows
+    rows = 64 * 32 * 8
     expect = ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
     assert n == expect
     assert _lib.decode_fwd(p, None, n, 0) == _lib.FA_ERR_WORKSPACE
@@ -228,10 +231,15 @@ def test_decode_workspace_rules(lib):
     assert "too small" in _lib.last_error()
     assert _lib.decode_fwd(p, FAKE + 4, n, 0) == _lib.FA_ERR_WORKSPACE
     # explicit chunk sizes change the requirement accordingly
-    p64 = _decode(chunk_keys=64)
-    _, n64 = _lib.decode_workspace_size(p64)
-    rows = 64 * 32 * 128
-    assert n64 == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    p128 = _decode(chunk_keys=128)
+    _, n128 = _lib.decode_workspace_size(p128)
+    rows = 64 * 32 * 64
+    assert n128 == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    # a small batch at low capacity gets shorter chunks (more workgroups)
+    ps = _decode(batch=2, cache_capacity=1000)
+    _, ns = _lib.decode_workspace_size(ps)
+    rows = 2 * 32 * 8          # 16 kv groups x ceil(1000/128) < 4096 -> 128-key chunks
+    assert ns == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
     # empty batch is a no-op needing no workspace
     p0 = _decode(batch=0)
     assert _lib.decode_workspace_size(p0) == (_lib.FA_OK, 0)

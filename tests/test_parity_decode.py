@@ -28,10 +28,11 @@ def test_workload5_decode_full():
     _case(workloads.make_workload(5), "decode B64 Hq32 Hkv8 d128 L U[512,8192]")
 
 
-@pytest.mark.parametrize("chunk", [0, 64, 128, 256])
+@pytest.mark.parametrize("chunk", [0, 128, 256, 512])
 def test_lengths_around_chunk_edges(chunk):
-    lengths = np.array([1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 600, 0, 1000],
-                       dtype=np.int32)
+    # edges of the 32-key tiles, the 128-key tile rounds of a workgroup and the chunks
+    lengths = np.array([1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384,
+                        385, 511, 512, 513, 600, 0, 1000], dtype=np.int32)
     dp = workloads.make_decode(50, len(lengths), 8, 2, 128, 1000, (1, 1000), "bf16",
                                lengths=lengths)
     _case(dp, f"lengths at chunk edges, chunk={chunk}", chunk_keys=chunk)
@@ -43,7 +44,7 @@ def test_gqa_groups(Hq, Hkv):
     _case(dp, f"GQA Hq{Hq} Hkv{Hkv}")
 
 
-@pytest.mark.parametrize("chunk", [0, 64, 256])
+@pytest.mark.parametrize("chunk", [0, 128, 512])
 def test_head_dim_64(chunk):
     dp = workloads.make_decode(52, 6, 12, 4, 64, 777, (1, 777), "bf16")
     _case(dp, "d64", chunk_keys=chunk)
@@ -71,7 +72,7 @@ def test_lengths_clamped_to_capacity():
 
 def test_chunk_sizes_agree():
     dp = workloads.make_decode(55, 8, 8, 2, 128, 2000, (1, 2000), "bf16")
-    outs = [run_decode(dp, chunk_keys=c) for c in (64, 128, 256)]
+    outs = [run_decode(dp, chunk_keys=c) for c in (128, 256, 512, 1024)]
     for o, l in outs[1:]:
         assert np.abs(o - outs[0][0]).max() <= 2e-2
         assert np.abs(l - outs[0][1]).max() <= 1e-3

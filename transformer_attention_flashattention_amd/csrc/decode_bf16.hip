@@ -5,23 +5,30 @@
 // nothing already in the cache is recomputed.  The work is a stream over the
 // cache, so the kernels are organised around HBM bandwidth, not MFMA:
 //
-// Split kernel -- one workgroup per (sequence, KV head, chunk of C keys):
-//   * every K and V row of the chunk is read from HBM exactly once and used
-//     for all query heads of its GQA group (query head h reads KV head
-//     h / group);
-//   * all of the chunk's K and V loads are issued up front as 16-byte vector
-//     loads (8 or 16 lanes cover one 256-byte row, so each wavefront-wide
-//     load instruction touches whole 128-byte segments), keeping many bytes
-//     in flight per CU;
-//   * scores q.k use the packed bf16 dot product (v_dot2_f32_bf16, fp32
-//     accumulate) and a 3-step DPP reduction inside each 8-lane row group;
-//   * the chunk's softmax statistics (max m, sum l, base-2 with the scale
-//     folded in) and its unnormalised P.V are written to the workspace.
-// Combine kernel -- one wavefront per (sequence, query head): merges the
+// Split kernel -- one workgroup (4 wavefronts) per (sequence, KV head, chunk
+// of keys).  Every K and V row of the chunk is read from HBM exactly once and
+// used for all query heads of its GQA group (query head h reads KV head
+// h / group).  Each wavefront walks its share of the chunk in tiles of 32 keys
+// (wavefront w takes tiles w, w+4, ...) and keeps the next tile's K and V
+// loads in flight (non-temporal 16-byte loads, whole 256-byte rows per group
+// of lanes) while it computes the current one, with its own running softmax:
+//   * scores: 16 dims per lane (two 16-byte pieces, each load instruction
+//     covering contiguous half rows), packed bf16 dot products (v_dot2_f32_bf16,
+//     fp32 accumulate) and a DPP sum over the lanes of a key;
+//   * running max per head, kept as a reference that only moves when a tile
+//     max passes it by 2^8 (base-2, scale folded in), so the accumulators are
+//     rescaled only then (the max correction of the hwcomputing.csdn.net page,
+//     section 2.2);
+//   * P leaves the score layout through a 32 x heads slot of LDS private to
+//     the wavefront and is read back in the value layout (8 dims per lane),
+//     where P.V accumulates in fp32 registers.
+// The four wavefronts merge their (max, sum, P.V) once per chunk through LDS
+// and write the chunk's partial to the workspace.
+// Combine kernel -- one workgroup per (sequence, query head): merges the
 //   chunk partials with the log-sum-exp rule (M = max m_c; L = sum 2^(m_c-M)
-//   l_c; O = sum 2^(m_c-M) O_c / L; LSE = ln 2 (M + log2 L)), which is the
-//   same max correction the running softmax uses within a chunk
-//   (hwcomputing.csdn.net page, section 2.2), and writes O (bf16) and LSE.
+//   l_c; O = sum 2^(m_c-M) O_c / L; LSE = ln 2 (M + log2 L)), the same max
+//   correction the running softmax uses within a chunk, and writes O (bf16)
+//   and LSE.
 #include "fa_internal.h"
 
 #include <cmath>
@@ -33,7 +40,10 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int NTHREADS = 256;
+constexpr int NWAVES = NTHREADS / 64;
+constexpr int KT = 32;                       // keys per wavefront tile
 constexpr float LN2 = 0.693147180559945309f;
+constexpr float RESCALE_THRESHOLD = 8.0f;    // log2 of the largest un-rescaled p
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
@@ -43,12 +53,50 @@ __device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
                                            __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Sum over the 8 lanes of an aligned group (every lane gets the total).
-__device__ __forceinline__ float sum8(float x) {
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+// Sum over the N lanes (N = 4 or 8) of an aligned group; every lane gets the total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);       // quad_perm [2,3,0,1]
+    if constexpr (N == 8) x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
     return x;
+}
+
+// Values of lanes l ^ 16 and l ^ 32, exchanged with the VALU lane swaps.
+__device__ __forceinline__ float xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    // lanes of even rows find the partner in the second result, odd rows in the first
+    return __builtin_bit_cast(float, (unsigned)(((threadIdx.x >> 4) & 1) ? r[0] : r[1]));
+}
+__device__ __forceinline__ float xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return __builtin_bit_cast(float, (unsigned)(((threadIdx.x >> 5) & 1) ? r[0] : r[1]));
+}
+// Value of lane l ^ 8 (DPP row_ror:8 inside each row of 16 lanes).
+__device__ __forceinline__ float xor8(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+// Value of lane (l + 4) mod 16 inside each row of 16 lanes (DPP row_ror:4).
+__device__ __forceinline__ float ror4(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+}
+// Max / sum over the lanes that share l % N (N = 4 or 8): the lane groups of
+// one key position in a layout with N lanes per key.
+template <int N>
+__device__ __forceinline__ float across_groups_max(float x) {
+    if constexpr (N == 4) x = fmaxf(x, ror4(x));
+    x = fmaxf(x, xor8(x));
+    x = fmaxf(x, xor16(x));
+    return fmaxf(x, xor32(x));
+}
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float x) {
+    if constexpr (N == 4) x += ror4(x);
+    x += xor8(x);
+    x += xor16(x);
+    return x + xor32(x);
 }
 
 // Keys [lo, L) of sequence b are visible to its decode query.
@@ -57,182 +105,255 @@ __device__ __forceinline__ void visible_range(const DecodeArgs &a, int b, int &l
     lo = (a.window_left > 0) ? max(0, L - a.window_left) : 0;
 }
 
-// D: head_dim; GT: query heads per workgroup; C: keys per chunk.
-template <int D, int GT, int C>
+__device__ __forceinline__ u32x4 load_nt(const unsigned short *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+
+// D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
+// a slice of it).  The chunk length a.chunk is a multiple of NWAVES * KT.
+template <int D, int GT>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
-    constexpr int DPL = D / 8;               // dims per lane in the score phase (8 lanes / key)
-    constexpr int KVEC = DPL / 8;            // 16-byte loads per key per lane (score phase)
-    constexpr int KPASS = NTHREADS / 8;      // keys per pass in the score phase
-    constexpr int NK = C / KPASS;            // keys per lane in the score phase
-    constexpr int LV = D / 8;                // lanes per key in the value phase
-    constexpr int VPASS = NTHREADS / LV;     // keys per pass in the value phase
-    constexpr int NV = C / VPASS;            // keys per lane in the value phase
-    static_assert(C % KPASS == 0 && C % VPASS == 0, "chunk size");
+    constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
+    constexpr int SKP = 64 / SL;             // keys per score pass
+    constexpr int SP = KT / SKP;             // score passes per tile
+    constexpr int VL = D / 8;                // value layout: lanes per key (8 dims each)
+    constexpr int VKP = 64 / VL;             // keys per value pass
+    constexpr int VP = KT / VKP;             // value passes per tile
+    static_assert(GT <= SL && (SL == 4 || SL == 8), "layout");
 
-    __shared__ __attribute__((aligned(16))) float sc[C * GT];          // scores, then p
-    __shared__ float red[2][NTHREADS / 64][GT];
-    __shared__ __attribute__((aligned(16))) float ored[VPASS][GT][D];  // value-phase partials
+    __shared__ __attribute__((aligned(16))) float pw[NWAVES][KT][GT];   // P, per wavefront
+    __shared__ __attribute__((aligned(16))) float mo[NWAVES][GT][D];    // merge: P.V
+    __shared__ float mml[NWAVES][GT][2];                                 // merge: (m, l)
 
-    const int chunk = blockIdx.x;
-    const int hg = blockIdx.y % a.head_groups;
-    const int kvh = blockIdx.y / a.head_groups;
+    // KV head (group slice) varies fastest across workgroup ids: workgroups
+    // dispatched together read the rows of all KV heads of one key range,
+    // which are interleaved in the BSHD cache.
+    const int hg = blockIdx.x % a.head_groups;
+    const int kvh = blockIdx.x / a.head_groups;
+    const int chunk = blockIdx.y;
     const int b = blockIdx.z;
     int lo, L;
     visible_range(a, b, lo, L);
+    const int C = a.chunk;
     const int c_lo = lo / C, c_hi = (L + C - 1) / C;
     if (chunk < c_lo || chunk >= c_hi) return;     // nothing visible in this chunk
     const int k0 = chunk * C;
     const int h0 = kvh * a.group + hg * GT;        // first query head of this workgroup
+    // keys this workgroup owns: the visible part of its chunk (never empty)
+    const int jlo = max(lo, k0), jhi = min(L, k0 + C);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // wavefront index, made provably uniform so that branches on it are scalar
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const unsigned short *Kp = (const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh;
     const unsigned short *Vp = (const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh;
+    const int s_key = lane / SL, s_sub = lane % SL;    // score layout
+    const int v_key = lane / VL, v_sub = lane % VL;    // value layout
+    const int my_g = s_sub < GT ? s_sub : 0;           // head whose P this lane produces
 
-    // ---- issue every K and V load of the chunk ----------------------------
-    const int ksub = tid & 7, kslot = tid >> 3;
-    u32x4 kr[NK][KVEC];
-#pragma unroll
-    for (int p = 0; p < NK; ++p) {
-        const int j = k0 + p * KPASS + kslot;
-        const bool ok = j >= lo && j < L;
-#pragma unroll
-        for (int v = 0; v < KVEC; ++v) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (ok) x = *(const u32x4 *)(Kp + (int64_t)j * a.k_ss + v * 64 + ksub * 8);
-            kr[p][v] = x;
-        }
-    }
-    const int vsub = tid % LV, vslot = tid / LV;
-    u32x4 vr[NV];
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-        const int j = k0 + p * VPASS + vslot;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (j >= lo && j < L) x = *(const u32x4 *)(Vp + (int64_t)j * a.v_ss + vsub * 8);
-        vr[p] = x;
-    }
-
-    // ---- query slices for the score phase (bf16 pairs) --------------------
-    unsigned qr[GT][KVEC][4];
+    // query slice of every head, the same 16 dims a lane holds of each key:
+    // dims 8 s_sub .. +8 and D/2 + 8 s_sub .. +8 (8 bf16 pairs)
+    unsigned qr[GT][8];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-        const unsigned short *qp = (const unsigned short *)a.q + b * a.q_sb + (h0 + g) * a.q_sh;
+        const unsigned short *qp = (const unsigned short *)a.q + b * a.q_sb + (h0 + g) * a.q_sh + s_sub * 8;
+        const u32x4 x0 = *(const u32x4 *)qp, x1 = *(const u32x4 *)(qp + D / 2);
 #pragma unroll
-        for (int v = 0; v < KVEC; ++v) {
-            const u32x4 x = *(const u32x4 *)(qp + v * 64 + ksub * 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qr[g][v][i] = x[i];
+        for (int i = 0; i < 4; ++i) {
+            qr[g][i] = x0[i];
+            qr[g][4 + i] = x1[i];
         }
     }
 
-    // ---- scores ------------------------------------------------------------
+    // running state (m, the reference, is uniform across the wavefront)
+    float m_ref[GT], o[GT][8];
+    float l_part = 0.f;                                // this lane's share of the sum of head my_g
 #pragma unroll
-    for (int p = 0; p < NK; ++p) {
-        const int jl = p * KPASS + kslot;
-        const int j = k0 + jl;
-        const bool ok = j >= lo && j < L;
-        float sg[GT];
+    for (int g = 0; g < GT; ++g) {
+        m_ref[g] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+    }
+    const float c2 = a.scale_log2;
+
+    // This wavefront's tiles t = 0 .. C/128 - 1 start at key base + 128 t; the
+    // ones holding a visible key form one contiguous range [ta, tb).
+    constexpr int STEP = NWAVES * KT;
+    const int ntl = C / STEP;
+    const int base = k0 + wave * KT;
+    auto tile_key0 = [&](int t) { return base + t * STEP; };
+    auto cdiv = [](int n) { return n <= 0 ? -((-n) / STEP) : (n + STEP - 1) / STEP; };
+    const int ta = max(0, cdiv(jlo - (KT - 1) - base));
+    const int tb = min(ntl, cdiv(jhi - base));
+    // Keys outside [jlo, jhi) load a clamped, valid row instead (finite data;
+    // the score mask then gives them p = 0), so every load is unconditional and
+    // the compiler can wait for exactly the current tile's loads.
+    u32x4 kb[2][SP][2], vb[2][VP];
+    auto load = [&](int t, u32x4 (&kt)[SP][2], u32x4 (&vt)[VP]) __attribute__((always_inline)) {
+        const int t0 = tile_key0(t);
+#pragma unroll
+        for (int p = 0; p < SP; ++p) {
+            const int j = min(max(t0 + p * SKP + s_key, jlo), jhi - 1);
+            // each load instruction covers one contiguous half of every row it touches
+            const unsigned short *src = Kp + (int64_t)j * a.k_ss + s_sub * 8;
+            kt[p][0] = load_nt(src);
+            kt[p][1] = load_nt(src + D / 2);
+        }
+#pragma unroll
+        for (int p = 0; p < VP; ++p) {
+            const int j = min(max(t0 + p * VKP + v_key, jlo), jhi - 1);
+            vt[p] = load_nt(Vp + (int64_t)j * a.v_ss + v_sub * 8);
+        }
+    };
+    auto compute = [&](int t, const u32x4 (&kt)[SP][2], const u32x4 (&vt)[VP]) __attribute__((always_inline)) {
+        const int t0 = tile_key0(t);
+        // scores of this lane's keys for every head
+        float s[SP][GT];
+#pragma unroll
+        for (int p = 0; p < SP; ++p) {
+            const int j = t0 + p * SKP + s_key;
+            const bool ok = j >= jlo && j < jhi;
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = dot2(kt[p][0][i], qr[g][i], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = dot2(kt[p][1][i], qr[g][4 + i], acc);
+                acc = group_sum<SL>(acc);
+                s[p][g] = ok ? acc : -INFINITY;
+            }
+        }
+        // tile max per head over the wavefront, then the lazy reference update
+        bool move = false;
+        float m_new[GT];
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
-            float acc = 0.f;
+            float mt = s[0][g];
 #pragma unroll
-            for (int v = 0; v < KVEC; ++v)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = dot2(kr[p][v][i], qr[g][v][i], acc);
-            sg[g] = sum8(acc);
+            for (int p = 1; p < SP; ++p) mt = fmaxf(mt, s[p][g]);
+            mt = across_groups_max<SL>(mt);
+            m_new[g] = fmaxf(m_ref[g], mt * c2);
+            move |= m_new[g] > m_ref[g] + RESCALE_THRESHOLD;
         }
-        if (ksub == 0) {
+        if (move) {                                  // uniform across the wavefront
+            float alpha_my = 1.f;
 #pragma unroll
-            for (int g = 0; g < GT; ++g) sc[jl * GT + g] = ok ? sg[g] : -INFINITY;
+            for (int g = 0; g < GT; ++g) {
+                const bool mv = m_new[g] > m_ref[g] + RESCALE_THRESHOLD;
+                const float alpha = mv ? __builtin_amdgcn_exp2f(m_ref[g] - m_new[g]) : 1.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+                if (g == my_g) alpha_my = alpha;
+                if (mv) m_ref[g] = m_new[g];
+            }
+            l_part *= alpha_my;
         }
-    }
-    __syncthreads();
+        // P of head my_g for this lane's keys, into the wavefront's LDS slot
+        float m_my = m_ref[0];
+#pragma unroll
+        for (int g = 1; g < GT; ++g) m_my = (my_g == g) ? m_ref[g] : m_my;
+        const float m_use = (m_my == -INFINITY) ? 0.f : m_my;
+#pragma unroll
+        for (int p = 0; p < SP; ++p) {
+            float sv = s[p][0];
+#pragma unroll
+            for (int g = 1; g < GT; ++g) sv = (my_g == g) ? s[p][g] : sv;
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -m_use));
+            if (s_sub < GT) {
+                l_part += pv;
+                pw[wave][p * SKP + s_key][s_sub] = pv;
+            }
+        }
+        // P.V in the value layout
+#pragma unroll
+        for (int p = 0; p < VP; ++p) {
+            float pg[GT];
+            const float *src = &pw[wave][p * VKP + v_key][0];
+            if constexpr (GT == 4) {
+                const float4 x = *(const float4 *)src;
+                pg[0] = x.x; pg[1] = x.y; pg[2] = x.z; pg[3] = x.w;
+            } else if constexpr (GT == 2) {
+                const float2 x = *(const float2 *)src;
+                pg[0] = x.x; pg[1] = x.y;
+            } else {
+                pg[0] = src[0];
+            }
+            float vf[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vf[2 * i] = bf_lo(vt[p][i]);
+                vf[2 * i + 1] = bf_hi(vt[p][i]);
+            }
+#pragma unroll
+            for (int g = 0; g < GT; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[g][e] = __builtin_fmaf(pg[g], vf[e], o[g][e]);
+        }
+    };
 
-    // ---- chunk softmax statistics per head ---------------------------------
-    // Thread t only ever touches entries of head t % GT.
-    constexpr int PER = (C * GT + NTHREADS - 1) / NTHREADS;
-    const int myg = tid % GT;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int idx = i * NTHREADS + tid;
-        if (idx < C * GT) mx = fmaxf(mx, sc[idx]);
+    // ---- tile loop: the next tile's loads are in flight during each compute --
+    // Loads are issued on every path, also for a tile past tb (its keys all
+    // clamp to row jhi-1: one cached row, no HBM traffic), and tiles go in
+    // pairs (a tile past tb has every key masked: p = 0 against finite rows),
+    // so each loop iteration is the same load/compute sequence and the
+    // compiler waits only for the tile in use.
+    load(ta, kb[0], vb[0]);
+    for (int t = ta; t < tb; t += 2) {
+        load(t + 1, kb[1], vb[1]);
+        compute(t, kb[0], vb[0]);
+        load(t + 2, kb[0], vb[0]);
+        compute(t + 1, kb[1], vb[1]);
     }
-#pragma unroll
-    for (int off = GT; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane < GT) red[0][wave][lane] = mx;
-    __syncthreads();
-    float m2 = red[0][0][myg];
-#pragma unroll
-    for (int w = 1; w < NTHREADS / 64; ++w) m2 = fmaxf(m2, red[0][w][myg]);
-    m2 *= a.scale_log2;                                   // base-2, scaled
-    const float m_use = (m2 == -INFINITY) ? 0.f : m2;
-    float ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int idx = i * NTHREADS + tid;
-        if (idx < C * GT) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[idx], a.scale_log2, -m_use));
-            sc[idx] = p;
-            ls += p;
-        }
-    }
-#pragma unroll
-    for (int off = GT; off < 64; off <<= 1) ls += __shfl_xor(ls, off);
-    if (lane < GT) red[1][wave][lane] = ls;
-    __syncthreads();
 
-    // ---- unnormalised P.V over the chunk -----------------------------------
-    float o[GT][8];
+    // ---- merge: lanes of a wavefront, then the four wavefronts ------------
+    // P.V: lanes with the same dims (v_sub) hold different keys
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-        const int jl = p * VPASS + vslot;
-        float pg[GT];
-#pragma unroll
-        for (int g = 0; g < GT; ++g) pg[g] = sc[jl * GT + g];
-        float vf[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vf[2 * i] = bf_lo(vr[p][i]);
-            vf[2 * i + 1] = bf_hi(vr[p][i]);
+        for (int e = 0; e < 8; ++e) {
+            float x = o[g][e];
+            if constexpr (VL == 8) x += xor8(x);
+            x += xor16(x);
+            x += xor32(x);
+            o[g][e] = x;
         }
+    // row sum of head my_g: lanes with the same s_sub hold different keys
+    const float lsum = across_groups_sum<SL>(l_part);
+    if (v_key == 0) {
 #pragma unroll
-        for (int g = 0; g < GT; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[g][e] = __builtin_fmaf(pg[g], vf[e], o[g][e]);
+        for (int g = 0; g < GT; ++g) {
+            *(float4 *)&mo[wave][g][v_sub * 8] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+            *(float4 *)&mo[wave][g][v_sub * 8 + 4] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+        }
     }
+    if (s_key == 0 && s_sub < GT) {
+        mml[wave][s_sub][0] = m_ref[0];
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-        *(float4 *)&ored[vslot][g][vsub * 8] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
-        *(float4 *)&ored[vslot][g][vsub * 8 + 4] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+        for (int g = 1; g < GT; ++g)
+            if (s_sub == g) mml[wave][s_sub][0] = m_ref[g];
+        mml[wave][s_sub][1] = lsum;
     }
     __syncthreads();
-
-    // ---- reduce over key slots and write the chunk partial -----------------
     for (int idx = tid; idx < GT * D; idx += NTHREADS) {
         const int g = idx / D, d = idx - (idx / D) * D;
-        float acc = 0.f;
+        float M = mml[0][g][0];
 #pragma unroll
-        for (int s = 0; s < VPASS; ++s) acc += ored[s][g][d];
+        for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, mml[w][g][0]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float acc = 0.f, lacc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            const float wt = __builtin_amdgcn_exp2f(mml[w][g][0] - M_use);
+            acc = __builtin_fmaf(wt, mo[w][g][d], acc);
+            lacc = __builtin_fmaf(wt, mml[w][g][1], lacc);
+        }
         const int64_t row = ((int64_t)b * a.heads_q + h0 + g) * a.max_chunks + chunk;
         a.ws_o[row * D + d] = acc;
-    }
-    if (tid < GT) {
-        float mm = red[0][0][tid];
-        float ll = red[1][0][tid];
-#pragma unroll
-        for (int w = 1; w < NTHREADS / 64; ++w) {
-            mm = fmaxf(mm, red[0][w][tid]);
-            ll += red[1][w][tid];
+        if (d == 0) {
+            a.ws_ml[row * 2 + 0] = M;
+            a.ws_ml[row * 2 + 1] = lacc;
         }
-        const int64_t row = ((int64_t)b * a.heads_q + h0 + tid) * a.max_chunks + chunk;
-        a.ws_ml[row * 2 + 0] = mm * a.scale_log2;
-        a.ws_ml[row * 2 + 1] = ll;
     }
 }
 
@@ -331,12 +452,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
 
 template <int D, int GT>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
-    const dim3 grid(a.max_chunks, a.heads_kv * a.head_groups, a.batch);
-    switch (a.chunk) {
-        case 64: hipLaunchKernelGGL((decode_split_kernel<D, GT, 64>), grid, dim3(NTHREADS), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((decode_split_kernel<D, GT, 128>), grid, dim3(NTHREADS), 0, s, a); break;
-        default: hipLaunchKernelGGL((decode_split_kernel<D, GT, 256>), grid, dim3(NTHREADS), 0, s, a); break;
-    }
+    const dim3 grid(a.heads_kv * a.head_groups, a.max_chunks, a.batch);
+    hipLaunchKernelGGL((decode_split_kernel<D, GT>), grid, dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -67,13 +67,12 @@ int decode_heads_per_wg(int group) {
 
 int decode_chunk(const fa_decode_params *p, int gt) {
     if (p->chunk_keys > 0) return p->chunk_keys;
-    // Largest chunk that still leaves enough workgroups to fill 256 CUs
-    // several times over when every sequence is at capacity.
+    // Longest chunk (fewest partials to combine) that still gives about 16
+    // workgroups per CU when every sequence is at capacity; every workgroup
+    // streams its chunk with four wavefronts of 32-key tiles.
     const long long groups = (long long)p->batch * p->heads_kv * (p->heads_q / p->heads_kv / gt);
-    // 128-key chunks measured fastest at capacity 8192 (more resident
-    // workgroups per CU than 256, fewer partials than 64).
-    int c = 128;
-    while (c > 64 && groups * ((p->cache_capacity + c - 1) / c) < 2048) c >>= 1;
+    int c = 1024;
+    while (c > fa::kDecodeChunkUnit && groups * ((p->cache_capacity + c - 1) / c) < 4096) c >>= 1;
     return c;
 }
 
@@ -93,8 +92,10 @@ fa_status validate_decode(const fa_decode_params *p) {
     if (p->cache_capacity < 1) return fail(FA_ERR_INVALID_ARG, "cache_capacity must be >= 1");
     if (p->window_left == 0 || p->window_left < -1)
         return fail(FA_ERR_INVALID_ARG, "window_left must be -1 or >= 1 (got %d)", p->window_left);
-    if (p->chunk_keys != 0 && p->chunk_keys != 64 && p->chunk_keys != 128 && p->chunk_keys != 256)
-        return fail(FA_ERR_UNSUPPORTED, "chunk_keys must be 0, 64, 128 or 256 (got %d)", p->chunk_keys);
+    if (p->chunk_keys != 0 &&
+        (p->chunk_keys < 0 || p->chunk_keys % fa::kDecodeChunkUnit != 0 || p->chunk_keys > 65536))
+        return fail(FA_ERR_UNSUPPORTED, "chunk_keys must be 0 or a multiple of %d up to 65536 (got %d)",
+                    fa::kDecodeChunkUnit, p->chunk_keys);
     if (p->reserved0 != 0) return fail(FA_ERR_INVALID_ARG, "reserved0 must be 0");
     FA_TRY(check_scale(p->softmax_scale));
     FA_TRY(check_strides("q", p->q_stride, 2, 8));
@@ -221,8 +222,7 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     if (workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     const int max_chunks = (p->cache_capacity + chunk - 1) / chunk;
-    if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL || p->batch > 65535 ||
-        (int64_t)p->heads_kv * (group / gt) > 65535)
+    if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL || p->batch > 65535 || max_chunks > 65535)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
     fa::DecodeArgs a{};

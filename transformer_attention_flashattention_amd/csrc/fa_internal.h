@@ -53,5 +53,6 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_w
 // Tile sizes the launchers use (also needed by the host for grid sizing).
 constexpr int kPrefillBM = 256;    // query rows per workgroup (bf16 path)
 constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
+constexpr int kDecodeChunkUnit = 128;  // decode chunks: 4 wavefronts x 32-key tiles
 
 }  // namespace fa
