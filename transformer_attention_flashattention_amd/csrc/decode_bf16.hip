@@ -8,10 +8,10 @@
 // Split kernel -- one workgroup (4 wavefronts) per (sequence, KV head, chunk
 // of keys).  Every K and V row of the chunk is read from HBM exactly once and
 // used for all query heads of its GQA group (query head h reads KV head
-// h / group).  Each wavefront walks its share of the chunk in tiles of 32 keys
-// (wavefront w takes tiles w, w+4, ...) and keeps the next tile's K and V
-// loads in flight (non-temporal 16-byte loads, whole 256-byte rows per group
-// of lanes) while it computes the current one, with its own running softmax:
+// h / group).  Each wavefront walks its share of the chunk in tiles of KT keys
+// (wavefront w takes tiles w, w+4, ...) and keeps the next NBUF-1 tiles' K and
+// V loads in flight (non-temporal 16-byte loads covering contiguous pieces of
+// each row) while it computes the current one, with its own running softmax:
 //   * scores: 16 dims per lane (two 16-byte pieces, each load instruction
 //     covering contiguous half rows), packed bf16 dot products (v_dot2_f32_bf16,
 //     fp32 accumulate) and a DPP sum over the lanes of a key;
@@ -19,7 +19,7 @@
 //     max passes it by 2^8 (base-2, scale folded in), so the accumulators are
 //     rescaled only then (the max correction of the hwcomputing.csdn.net page,
 //     section 2.2);
-//   * P leaves the score layout through a 32 x heads slot of LDS private to
+//   * P leaves the score layout through a KT x heads slot of LDS private to
 //     the wavefront and is read back in the value layout (8 dims per lane),
 //     where P.V accumulates in fp32 registers.
 // The four wavefronts merge their (max, sum, P.V) once per chunk through LDS
@@ -41,7 +41,14 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
-constexpr int KT = 32;                       // keys per wavefront tile
+#ifndef DECODE_KT
+#define DECODE_KT 16
+#endif
+#ifndef DECODE_NBUF
+#define DECODE_NBUF 4
+#endif
+constexpr int KT = DECODE_KT;                // keys per wavefront tile
+constexpr int NBUF = DECODE_NBUF;            // tiles held in registers: 1 computing, NBUF-1 in flight
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;    // log2 of the largest un-rescaled p
 
@@ -105,12 +112,22 @@ __device__ __forceinline__ void visible_range(const DecodeArgs &a, int b, int &l
     lo = (a.window_left > 0) ? max(0, L - a.window_left) : 0;
 }
 
-__device__ __forceinline__ u32x4 load_nt(const unsigned short *p) {
-    return __builtin_nontemporal_load((const u32x4 *)p);
+// The visible keys of a sequence are cut into n = ceil((L - lo) / a.chunk)
+// chunks of equal length len (a multiple of 128, at most a.chunk); chunk c
+// covers [lo + c len, min(L, lo + (c + 1) len)) and is never empty.  Equal
+// chunks keep the workgroups of one sequence equally long.
+__device__ __forceinline__ void chunking(const DecodeArgs &a, int lo, int L, int &n, int &len) {
+    const int Lv = L - lo;
+    n = (Lv + a.chunk - 1) / a.chunk;
+    len = n > 0 ? (((Lv + n - 1) / n + kDecodeChunkUnit - 1) / kDecodeChunkUnit) * kDecodeChunkUnit : 0;
+}
+
+__device__ __forceinline__ u32x4 load_nt(const char *base, unsigned off) {
+    return __builtin_nontemporal_load((const u32x4 *)(base + off));
 }
 
 // D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
-// a slice of it).  The chunk length a.chunk is a multiple of NWAVES * KT.
+// a slice of it).  Chunk lengths are multiples of NWAVES * KT.
 template <int D, int GT>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
@@ -120,33 +137,69 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int VKP = 64 / VL;             // keys per value pass
     constexpr int VP = KT / VKP;             // value passes per tile
     static_assert(GT <= SL && (SL == 4 || SL == 8), "layout");
+    static_assert(kDecodeChunkUnit % (NWAVES * KT) == 0, "chunks hold whole tile rounds");
 
     __shared__ __attribute__((aligned(16))) float pw[NWAVES][KT][GT];   // P, per wavefront
     __shared__ __attribute__((aligned(16))) float mo[NWAVES][GT][D];    // merge: P.V
     __shared__ float mml[NWAVES][GT][2];                                 // merge: (m, l)
 
-    // KV head (group slice) varies fastest across workgroup ids: workgroups
-    // dispatched together read the rows of all KV heads of one key range,
-    // which are interleaved in the BSHD cache.
-    const int hg = blockIdx.x % a.head_groups;
-    const int kvh = blockIdx.x / a.head_groups;
-    const int chunk = blockIdx.y;
-    const int b = blockIdx.z;
-    int lo, L;
-    visible_range(a, b, lo, L);
-    const int C = a.chunk;
-    const int c_lo = lo / C, c_hi = (L + C - 1) / C;
-    if (chunk < c_lo || chunk >= c_hi) return;     // nothing visible in this chunk
-    const int k0 = chunk * C;
-    const int h0 = kvh * a.group + hg * GT;        // first query head of this workgroup
-    // keys this workgroup owns: the visible part of its chunk (never empty)
-    const int jlo = max(lo, k0), jhi = min(L, k0 + C);
-
+    // Work items are the (sequence, chunk) pairs that exist, in that order,
+    // each taken by heads_kv * head_groups consecutive workgroups: KV head
+    // (group slice) varies fastest, so workgroups dispatched together read the
+    // rows of all KV heads of one key range (interleaved in the BSHD cache),
+    // and consecutive items sweep the cache in address order.  The grid is
+    // sized for every sequence at capacity; workgroups past the last item exit.
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int slots = a.heads_kv * a.head_groups;
+    const int item = blockIdx.x / slots;
+    const int slot = blockIdx.x - item * slots;
+    const int hg = slot % a.head_groups;
+    const int kvh = slot / a.head_groups;
+    int b = -1, chunk = 0;
+    {
+        int before = 0;                            // items of sequences b0 - 1 and below
+        for (int b0 = 0; b0 < a.batch; b0 += 64) {
+            int n = 0;
+            if (b0 + lane < a.batch) {
+                int lo_, L_, len_;
+                visible_range(a, b0 + lane, lo_, L_);
+                chunking(a, lo_, L_, n, len_);
+            }
+            int incl = n;                          // inclusive scan over the wavefront
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            const int excl = before + incl - n;
+            const unsigned long long hit = __ballot(n > 0 && item >= excl && item < excl + n);
+            if (hit) {
+                const int src = __ffsll((long long)hit) - 1;
+                b = b0 + src;
+                chunk = item - __shfl(excl, src);
+                break;
+            }
+            before += __shfl(incl, 63);
+        }
+    }
+    if (b < 0) return;                             // past the last work item
+    b = __builtin_amdgcn_readfirstlane(b);         // uniform (shuffle results are not provably so)
+    chunk = __builtin_amdgcn_readfirstlane(chunk);
+    int lo, L, nchunks, C;
+    visible_range(a, b, lo, L);
+    chunking(a, lo, L, nchunks, C);
+    const int k0 = lo + chunk * C;
+    const int h0 = kvh * a.group + hg * GT;        // first query head of this workgroup
+    // keys this workgroup owns (never empty)
+    const int jlo = k0, jhi = min(L, k0 + C);
+
     // wavefront index, made provably uniform so that branches on it are scalar
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const unsigned short *Kp = (const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh;
-    const unsigned short *Vp = (const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const char *Kp = (const char *)((const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh);
+    const char *Vp = (const char *)((const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh);
+    // row offsets within one sequence fit 32 bits (checked on the host)
+    const unsigned k_row = (unsigned)a.k_ss * 2u, v_row = (unsigned)a.v_ss * 2u;
     const int s_key = lane / SL, s_sub = lane % SL;    // score layout
     const int v_key = lane / VL, v_sub = lane % VL;    // value layout
     const int my_g = s_sub < GT ? s_sub : 0;           // head whose P this lane produces
@@ -188,21 +241,21 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     // Keys outside [jlo, jhi) load a clamped, valid row instead (finite data;
     // the score mask then gives them p = 0), so every load is unconditional and
     // the compiler can wait for exactly the current tile's loads.
-    u32x4 kb[2][SP][2], vb[2][VP];
+    u32x4 kb[NBUF][SP][2], vb[NBUF][VP];
     auto load = [&](int t, u32x4 (&kt)[SP][2], u32x4 (&vt)[VP]) __attribute__((always_inline)) {
         const int t0 = tile_key0(t);
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
             const int j = min(max(t0 + p * SKP + s_key, jlo), jhi - 1);
             // each load instruction covers one contiguous half of every row it touches
-            const unsigned short *src = Kp + (int64_t)j * a.k_ss + s_sub * 8;
-            kt[p][0] = load_nt(src);
-            kt[p][1] = load_nt(src + D / 2);
+            const unsigned off = (unsigned)j * k_row + s_sub * 16;
+            kt[p][0] = load_nt(Kp, off);
+            kt[p][1] = load_nt(Kp, off + D);
         }
 #pragma unroll
         for (int p = 0; p < VP; ++p) {
             const int j = min(max(t0 + p * VKP + v_key, jlo), jhi - 1);
-            vt[p] = load_nt(Vp + (int64_t)j * a.v_ss + v_sub * 8);
+            vt[p] = load_nt(Vp, (unsigned)j * v_row + v_sub * 16);
         }
     };
     auto compute = [&](int t, const u32x4 (&kt)[SP][2], const u32x4 (&vt)[VP]) __attribute__((always_inline)) {
@@ -232,7 +285,8 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             float mt = s[0][g];
 #pragma unroll
             for (int p = 1; p < SP; ++p) mt = fmaxf(mt, s[p][g]);
-            mt = across_groups_max<SL>(mt);
+            mt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                __builtin_bit_cast(int, across_groups_max<SL>(mt))));
             m_new[g] = fmaxf(m_ref[g], mt * c2);
             move |= m_new[g] > m_ref[g] + RESCALE_THRESHOLD;
         }
@@ -292,18 +346,20 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         }
     };
 
-    // ---- tile loop: the next tile's loads are in flight during each compute --
-    // Loads are issued on every path, also for a tile past tb (its keys all
+    // ---- tile loop: NBUF-1 tiles' loads are in flight during each compute ---
+    // Loads are issued on every path, also for tiles past tb (their keys all
     // clamp to row jhi-1: one cached row, no HBM traffic), and tiles go in
-    // pairs (a tile past tb has every key masked: p = 0 against finite rows),
-    // so each loop iteration is the same load/compute sequence and the
-    // compiler waits only for the tile in use.
-    load(ta, kb[0], vb[0]);
-    for (int t = ta; t < tb; t += 2) {
-        load(t + 1, kb[1], vb[1]);
-        compute(t, kb[0], vb[0]);
-        load(t + 2, kb[0], vb[0]);
-        compute(t + 1, kb[1], vb[1]);
+    // groups of NBUF (a tile past tb has every key masked: p = 0 against
+    // finite rows), so each loop iteration is the same load/compute sequence
+    // and the compiler waits only for the tile in use.
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load(ta + i, kb[i], vb[i]);
+    for (int t = ta; t < tb; t += NBUF) {
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i) {
+            load(t + i + NBUF - 1, kb[(i + NBUF - 1) % NBUF], vb[(i + NBUF - 1) % NBUF]);
+            compute(t + i, kb[i], vb[i]);
+        }
     }
 
     // ---- merge: lanes of a wavefront, then the four wavefronts ------------
@@ -375,12 +431,11 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
     const int bh = blockIdx.x;
     const int b = bh / a.heads_q, h = bh - (bh / a.heads_q) * a.heads_q;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int lo, L;
+    int lo, L, n, len;
     visible_range(a, b, lo, L);
-    const int C = a.chunk;
-    const int c_lo = lo / C, c_hi = (L > lo) ? (L + C - 1) / C : c_lo;
-    const int n = c_hi - c_lo;
-    const int64_t base = ((int64_t)b * a.heads_q + h) * a.max_chunks + c_lo;
+    chunking(a, lo, L, n, len);
+    (void)len;
+    const int64_t base = ((int64_t)b * a.heads_q + h) * a.max_chunks;
 
     float M = -INFINITY;
     for (int j = lane; j < n; j += 64) M = fmaxf(M, a.ws_ml[(base + j) * 2]);
@@ -452,7 +507,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
 
 template <int D, int GT>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
-    const dim3 grid(a.heads_kv * a.head_groups, a.max_chunks, a.batch);
+    const dim3 grid((unsigned)(a.heads_kv * a.head_groups) * a.batch * a.max_chunks);
     hipLaunchKernelGGL((decode_split_kernel<D, GT>), grid, dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }

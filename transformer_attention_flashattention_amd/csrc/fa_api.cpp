@@ -7,6 +7,7 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -222,7 +223,11 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     if (workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     const int max_chunks = (p->cache_capacity + chunk - 1) / chunk;
-    if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL || p->batch > 65535 || max_chunks > 65535)
+    // the split kernel addresses the rows of one sequence with 32-bit byte offsets
+    if ((int64_t)p->cache_capacity * std::max(p->k_stride[1], p->v_stride[1]) * 2 > 0xffffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "cache_capacity x seq stride exceeds 4 GiB per sequence");
+    if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL ||
+        (int64_t)p->heads_kv * (group / gt) * p->batch * max_chunks > 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
     fa::DecodeArgs a{};
