@@ -217,6 +217,20 @@ def test_decode_validation(lib, kw, status, needle):
         assert st2 == status
 
 
+def test_decode_rejects_cache_rows_beyond_32bit_offsets(lib):
+    # the split kernel addresses one sequence's rows with 32-bit byte offsets
+    p = _decode(batch=1, cache_capacity=1 << 22,
+                k_stride=[(1 << 22) * 8 * 128, 8 * 128, 128],
+                v_stride=[(1 << 22) * 8 * 128, 8 * 128, 128])
+    assert _lib.decode_fwd(p, FAKE, 1 << 40, 0) == _lib.FA_ERR_UNSUPPORTED
+    assert "4 GiB" in _lib.last_error()
+    p = _decode(batch=1, cache_capacity=1 << 20,
+                k_stride=[(1 << 20) * 8 * 128, 8 * 128, 128],
+                v_stride=[(1 << 20) * 8 * 128, 8 * 128, 128])
+    st, n = _lib.decode_workspace_size(p)
+    assert st == _lib.FA_OK and n > 0
+
+
 def test_decode_workspace_rules(lib):
     p = _decode()
     st, n = _lib.decode_workspace_size(p)

@@ -21,7 +21,8 @@
 //     section 2.2);
 //   * P leaves the score layout through a KT x heads slot of LDS private to
 //     the wavefront and is read back in the value layout (8 dims per lane),
-//     where P.V accumulates in fp32 registers.
+//     where P.V accumulates in fp32 registers (packed bf16 dot products over
+//     pairs of keys; P enters that product in bf16, its row sum in fp32).
 // The four wavefronts merge their (max, sum, P.V) once per chunk through LDS
 // and write the chunk's partial to the workspace.
 // Combine kernel -- one workgroup per (sequence, query head): merges the
@@ -42,18 +43,23 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
 #ifndef DECODE_KT
-#define DECODE_KT 16
+#define DECODE_KT 32
 #endif
 #ifndef DECODE_NBUF
-#define DECODE_NBUF 4
+#define DECODE_NBUF 2
 #endif
 constexpr int KT = DECODE_KT;                // keys per wavefront tile
 constexpr int NBUF = DECODE_NBUF;            // tiles held in registers: 1 computing, NBUF-1 in flight
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;    // log2 of the largest un-rescaled p
 
-__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(unsigned, r);
+}
 
 __device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -319,30 +325,42 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 pw[wave][p * SKP + s_key][s_sub] = pv;
             }
         }
-        // P.V in the value layout
+        // P.V in the value layout, two keys at a time: a lane holds the same 8
+        // dims of keys p and p+1 (passes p, p+1); v_perm_b32 pairs their values
+        // per dim and v_dot2_f32_bf16 multiplies them with the pair of P values
+        // (bf16, as for the matrix product of the prefill; fp32 accumulate)
+        static_assert(VP % 2 == 0, "value passes come in pairs");
 #pragma unroll
-        for (int p = 0; p < VP; ++p) {
-            float pg[GT];
-            const float *src = &pw[wave][p * VKP + v_key][0];
+        for (int p = 0; p < VP; p += 2) {
+            float pa[GT], pb[GT];
+            const float *src0 = &pw[wave][p * VKP + v_key][0];
+            const float *src1 = &pw[wave][(p + 1) * VKP + v_key][0];
             if constexpr (GT == 4) {
-                const float4 x = *(const float4 *)src;
-                pg[0] = x.x; pg[1] = x.y; pg[2] = x.z; pg[3] = x.w;
+                const float4 x = *(const float4 *)src0, y = *(const float4 *)src1;
+                pa[0] = x.x; pa[1] = x.y; pa[2] = x.z; pa[3] = x.w;
+                pb[0] = y.x; pb[1] = y.y; pb[2] = y.z; pb[3] = y.w;
             } else if constexpr (GT == 2) {
-                const float2 x = *(const float2 *)src;
-                pg[0] = x.x; pg[1] = x.y;
+                const float2 x = *(const float2 *)src0, y = *(const float2 *)src1;
+                pa[0] = x.x; pa[1] = x.y;
+                pb[0] = y.x; pb[1] = y.y;
             } else {
-                pg[0] = src[0];
+                pa[0] = src0[0];
+                pb[0] = src1[0];
             }
-            float vf[8];
+            unsigned pp[GT];
+#pragma unroll
+            for (int g = 0; g < GT; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                vf[2 * i] = bf_lo(vt[p][i]);
-                vf[2 * i + 1] = bf_hi(vt[p][i]);
+                const unsigned va = vt[p][i], vb = vt[p + 1][i];                 // dims 2i, 2i+1
+                const unsigned even = __builtin_amdgcn_perm(vb, va, 0x05040100u);  // (va.lo, vb.lo)
+                const unsigned odd = __builtin_amdgcn_perm(vb, va, 0x07060302u);   // (va.hi, vb.hi)
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    o[g][2 * i] = dot2(pp[g], even, o[g][2 * i]);
+                    o[g][2 * i + 1] = dot2(pp[g], odd, o[g][2 * i + 1]);
+                }
             }
-#pragma unroll
-            for (int g = 0; g < GT; ++g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[g][e] = __builtin_fmaf(pg[g], vf[e], o[g][e]);
         }
     };
 
