@@ -25,7 +25,7 @@
 //     pairs of keys; P enters that product in bf16, its row sum in fp32).
 // The four wavefronts merge their (max, sum, P.V) once per chunk through LDS
 // and write the chunk's partial to the workspace.
-// Combine kernel -- one workgroup per (sequence, query head): merges the
+// Combine kernel -- one wavefront per (sequence, query head): merges the
 //   chunk partials with the log-sum-exp rule (M = max m_c; L = sum 2^(m_c-M)
 //   l_c; O = sum 2^(m_c-M) O_c / L; LSE = ln 2 (M + log2 L)), the same max
 //   correction the running softmax uses within a chunk, and writes O (bf16)
@@ -431,32 +431,36 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-// One workgroup of 4 wavefronts per (sequence, query head).  Every lane of
-// every wavefront holds the (m, l) of one chunk (64 chunks per pass), so each
-// wavefront derives the global max and all weights on its own; wavefront w
-// then sums chunks w, w+4, w+8, ... with all of its partial-O loads issued
-// before the first use, and the four partial sums meet in LDS.  Each
-// (sequence, head) therefore costs about one memory round trip per 64 chunks.
+// One wavefront per (sequence, query head), four per workgroup.  The partial
+// P.V rows of the first 8 chunks are loaded before anything else, together
+// with every chunk's (m, l), so a sequence with at most 8 chunks (the usual
+// case: chunks are up to 1024 keys) costs one memory round trip; longer ones
+// loop over further groups of 8.  Each lane owns D / 64 dims of O.
 constexpr int COMBINE_THREADS = 256;
-constexpr int COMBINE_UNROLL = 16;   // chunks per wavefront per pass (64 / 4)
+constexpr int COMBINE_GROUP = 8;     // partial rows loaded per round trip
 
 template <int D>
 __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeArgs a) {
-    constexpr int DPL = (D + 63) / 64;       // dims per lane
-    __shared__ float part[COMBINE_THREADS / 64][D];
-    __shared__ float lpart[COMBINE_THREADS / 64];
-
-    const int bh = blockIdx.x;
+    constexpr int DPL = D / 64;              // dims per lane
+    const int lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * (COMBINE_THREADS / 64) + (threadIdx.x >> 6);
+    if (bh >= a.batch * a.heads_q) return;
     const int b = bh / a.heads_q, h = bh - (bh / a.heads_q) * a.heads_q;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int lo, L, n, len;
     visible_range(a, b, lo, L);
     chunking(a, lo, L, n, len);
     (void)len;
     const int64_t base = ((int64_t)b * a.heads_q + h) * a.max_chunks;
+    const float *wo = a.ws_o + base * D + lane * DPL;
+    const float *wml = a.ws_ml + base * 2;
 
+    float ov[COMBINE_GROUP][DPL];
+#pragma unroll
+    for (int u = 0; u < COMBINE_GROUP; ++u)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) ov[u][i] = u < n ? wo[(int64_t)u * D + i] : 0.f;
     float M = -INFINITY;
-    for (int j = lane; j < n; j += 64) M = fmaxf(M, a.ws_ml[(base + j) * 2]);
+    for (int j = lane; j < n; j += 64) M = fmaxf(M, wml[2 * j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float M_use = (M == -INFINITY) ? 0.f : M;
@@ -464,63 +468,35 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
     float acc[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
-    float Lsum = 0.f;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        // partial O rows of this wavefront's chunks in this pass: loads first
-        float ov[COMBINE_UNROLL][DPL];
+    float Lsum = 0.f;                        // the same in every lane
+    for (int j0 = 0; j0 < n; j0 += COMBINE_GROUP) {
+        if (j0 > 0) {
 #pragma unroll
-        for (int u = 0; u < COMBINE_UNROLL; ++u) {
-            const int j = j0 + wave + 4 * u;
+            for (int u = 0; u < COMBINE_GROUP; ++u)
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) {
-                const int d = lane * DPL + i;
-                ov[u][i] = (j < n && d < D) ? a.ws_o[(base + j) * D + d] : 0.f;
+                for (int i = 0; i < DPL; ++i) ov[u][i] = j0 + u < n ? wo[(int64_t)(j0 + u) * D + i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < COMBINE_GROUP; ++u) {
+            if (j0 + u < n) {
+                const float w = __builtin_amdgcn_exp2f(wml[2 * (j0 + u)] - M_use);
+                Lsum = __builtin_fmaf(w, wml[2 * (j0 + u) + 1], Lsum);
+#pragma unroll
+                for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(w, ov[u][i], acc[i]);
             }
         }
-        const int jl = j0 + lane;
-        float w = 0.f, lw = 0.f;
-        if (jl < n) {
-            w = __builtin_amdgcn_exp2f(a.ws_ml[(base + jl) * 2] - M_use);
-            lw = w * a.ws_ml[(base + jl) * 2 + 1];
-        }
-        Lsum += lw;
-#pragma unroll
-        for (int u = 0; u < COMBINE_UNROLL; ++u) {
-            const float wc = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), wave + 4 * u));
-#pragma unroll
-            for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(wc, ov[u][i], acc[i]);
-        }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) Lsum += __shfl_xor(Lsum, off);
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-        const int d = lane * DPL + i;
-        if (d < D) part[wave][d] = acc[i];
-    }
-    if (lane == 0) lpart[wave] = Lsum;
-    __syncthreads();
-    if (wave != 0) return;
 
-    // every wavefront summed all chunk weights, so any lpart entry is the total
-    const float Ltot = lpart[0];
-    const bool ok = Ltot > 0.f;
-    const float inv = ok ? 1.f / Ltot : 0.f;
-    unsigned short *orow = (unsigned short *)a.o + b * a.o_sb + h * a.o_sh;
+    const bool ok = Lsum > 0.f;
+    const float inv = ok ? 1.f / Lsum : 0.f;
+    unsigned short *orow = (unsigned short *)a.o + b * a.o_sb + h * a.o_sh + lane * DPL;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
-        const int d = lane * DPL + i;
-        if (d < D) {
-            float v = part[0][d];
-#pragma unroll
-            for (int w2 = 1; w2 < COMBINE_THREADS / 64; ++w2) v += part[w2][d];
-            const __bf16 x = (__bf16)(v * inv);
-            orow[d] = __builtin_bit_cast(unsigned short, x);
-        }
+        const __bf16 x = (__bf16)(acc[i] * inv);
+        orow[i] = __builtin_bit_cast(unsigned short, x);
     }
     if (a.lse && lane == 0)
-        a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Ltot)) * LN2 : -INFINITY;
+        a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Lsum)) * LN2 : -INFINITY;
 }
 
 template <int D, int GT>
@@ -539,7 +515,9 @@ hipError_t launch_all(const DecodeArgs &a, int gt, hipStream_t s) {
         default: e = launch_split<D, 4>(a, s); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.batch * a.heads_q), dim3(COMBINE_THREADS), 0,
+    const int per_wg = COMBINE_THREADS / 64;
+    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((a.batch * a.heads_q + per_wg - 1) / per_wg),
+                       dim3(COMBINE_THREADS), 0,
                        s, a);
     return hipGetLastError();
 }
