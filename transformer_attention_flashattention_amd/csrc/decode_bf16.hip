@@ -43,7 +43,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
 #ifndef DECODE_KT
-#define DECODE_KT 32
+#define DECODE_KT 16
 #endif
 #ifndef DECODE_NBUF
 #define DECODE_NBUF 2
