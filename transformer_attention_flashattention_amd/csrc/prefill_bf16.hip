@@ -60,12 +60,16 @@
 //   free of bank conflicts); the swizzle is applied on the global side of the
 //   direct loads, which always write 1 KiB contiguous per wavefront.
 //
-// Softmax bookkeeping: the row reference max only moves when the running max
-// exceeds it by more than 2^8 (in the base-2 exponent domain); until then P
-// is taken against the old reference, so O, the row sum and P always share
-// one reference and the result is exact -- only the rescale work is skipped.
-// The row sum adds the fp32 P values (before their bf16 rounding for the PV
-// product), so LSE carries only fp32 rounding.
+// Softmax bookkeeping: P is taken against a per-row reference, not the exact
+// running max.  A tile first computes P against the current reference; only
+// when some row has no reference yet, or a lane's P sum for the tile passes
+// 2^16 (so no P can have passed it), does the wavefront compute the exact row
+// max and move the reference of the rows whose max passed it by more than 8
+// in the base-2 exponent domain (a factor 2^8), rescale O and the row sum,
+// and recompute P.  O, the row sum and P always share one reference, so the
+// result is exact up to rounding; the row max and the rescale work are
+// skipped on almost every tile.  The row sum adds the fp32 P values (before
+// their bf16 rounding for the PV product), so LSE carries only fp32 rounding.
 #include "fa_internal.h"
 
 #include <climits>
@@ -89,6 +93,9 @@ constexpr int NTHREADS = NWAVES * 64;
 static_assert(BM == NWAVES * 32, "one 32-row block per wavefront");
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the largest un-rescaled p
+// Fast-path bound on the P values of one lane's share of a tile: 2^16 keeps
+// bf16 P and the fp32 accumulators far from overflow.
+constexpr float FAST_BOUND = 65536.0f;
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
@@ -385,15 +392,39 @@ void prefill_bf16_kernel(PrefillArgs a) {
                     s[sb][r] = (key >= vis_lo && key < vis_hi) ? s[sb][r] : -INFINITY;
                 }
         }
-        float mx = s[0][0];
+        // P of this tile against the current reference (fast path: no row max)
+        auto exps = [&](float m_use, float &psum) __attribute__((always_inline)) {
+            psum = 0.f;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_ref, mx * c2);
-        if (__ballot(m_new > m_ref + RESCALE_THRESHOLD)) {
-            // move the reference: at least one row of this wavefront grew too far
+                for (int tt = 0; tt < 2; ++tt) {
+                    u32x4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i], c2, -m_use));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i + 1], c2, -m_use));
+                        w[i] = pack_bf16x2(p0, p1);
+                        psum += p0 + p1;
+                    }
+                    pb[sb * 2 + tt] = __builtin_bit_cast(bf16x8, w);
+                }
+        };
+        float psum;
+        exps((m_ref == -INFINITY) ? 0.f : m_ref, psum);
+        // The fast path stands unless a row has no reference yet, or some P of
+        // this lane may exceed FAST_BOUND (its sum does; this also catches an
+        // overflow to inf).  Then the wavefront takes the exact row
+        // max, moves the reference where it grew past the threshold, rescales
+        // O and the row sum, and recomputes P.
+        if (__ballot(m_ref == -INFINITY || !(psum <= FAST_BOUND))) {
+            float mx = s[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+            mx = pair_max(mx);
+            const float m_new = fmaxf(m_ref, mx * c2);
             const float m_to = (m_new > m_ref + RESCALE_THRESHOLD) ? m_new : m_ref;
             // 1 for rows that keep their reference (also when both are -inf),
             // 0 when the old reference is -inf (nothing accumulated yet)
@@ -404,23 +435,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
             for (int jd = 0; jd < DBLK; ++jd)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[jd][r] *= alpha;
+            exps((m_ref == -INFINITY) ? 0.f : m_ref, psum);
         }
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-        float psum = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                u32x4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i], c2, -m_use));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i + 1], c2, -m_use));
-                    w[i] = pack_bf16x2(p0, p1);
-                    psum += p0 + p1;
-                }
-                pb[sb * 2 + tt] = __builtin_bit_cast(bf16x8, w);
-            }
         l_run += psum;
     };
 
