@@ -70,6 +70,21 @@ def test_lengths_clamped_to_capacity():
     check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "clamped lengths")
 
 
+def test_reference_moves_under_growing_scores():
+    """Keys whose scores grow by ~20 base-2 units per 32 keys force the running
+    reference of every wavefront to move on most tiles (and every chunk's
+    partial to sit at a very different max, which the combine must merge)."""
+    dp = workloads.make_decode(57, 4, 8, 2, 128, 1500, (600, 1500), "bf16")
+    q = 0.1 * workloads.bf16_bits_to_f32(dp.q).astype(np.float64) + 1.0
+    k = workloads.bf16_bits_to_f32(dp.k_cache).astype(np.float64)
+    cap = k.shape[1]
+    g = 20.0 * np.arange(cap) / 32.0 / (dp.scale * np.log2(np.e) * 128)
+    k = np.where(np.isnan(k), k, 0.1 * k + g[None, :, None, None])
+    dp.q = workloads.f32_to_bf16_bits(q.astype(np.float32))
+    dp.k_cache = workloads.f32_to_bf16_bits(k.astype(np.float32))
+    _case(dp, "growing scores")
+
+
 def test_chunk_sizes_agree():
     dp = workloads.make_decode(55, 8, 8, 2, 128, 2000, (1, 2000), "bf16")
     outs = [run_decode(dp, chunk_keys=c) for c in (128, 256, 512, 1024)]

@@ -147,6 +147,34 @@ def test_large_score_offset_is_stable():
     _case(p, "large score offsets")
 
 
+def _growing_scores(p, rate):
+    """Rewrite Q and K so that, for even query rows, scale*q.k grows by about
+    `rate` (base-2 exponent units) per 64 keys along the key axis, and falls as
+    fast for odd rows: rows of one wavefront then move their softmax
+    reference at different tiles."""
+    B, Nq, Hq, d = p.q.shape
+    Nk, Hkv = p.k.shape[1], p.k.shape[2]
+    q = 0.1 * workloads.bf16_bits_to_f32(p.q).astype(np.float64)
+    k = 0.1 * workloads.bf16_bits_to_f32(p.k).astype(np.float64)
+    sign = np.where(np.arange(Nq) % 2 == 0, 1.0, -1.0)[None, :, None, None]
+    q += sign
+    # scale*log2(e)*d*g per key; g grows linearly with the key index
+    g = rate * np.arange(Nk) / 64.0 / (p.scale * np.log2(np.e) * d)
+    k += g[None, :, None, None]
+    p.q = workloads.f32_to_bf16_bits(q.astype(np.float32))
+    p.k = workloads.f32_to_bf16_bits(k.astype(np.float32))
+    return p
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_reference_moves_under_growing_scores(causal):
+    """Scores that grow (or fall) by ~20 base-2 units per tile force the softmax
+    reference of half the rows of every wavefront to move on most tiles."""
+    p = _growing_scores(workloads.make_prefill(21, 1, 1000, 1000, 2, 2, 128, "bf16",
+                                               causal=causal), 20.0)
+    _case(p, f"growing scores causal={causal}")
+
+
 # ---------------------------------------------------------------------------
 # Padding, poisoning, canaries, determinism, layouts, memory
 # ---------------------------------------------------------------------------

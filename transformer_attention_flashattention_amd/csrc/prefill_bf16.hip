@@ -126,6 +126,17 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(unsigned, r);
 }
 
+// Workgroup barrier of the phase loop.  __syncthreads() would also drain
+// every outstanding vector-memory operation of the wavefront (its fence is
+// lowered with vmcnt(0)), i.e. wait for the direct-to-LDS loads issued at the
+// start of the phase, which no reader needs before the next odd phase; this
+// barrier only drains the wavefront's LDS reads.  Where the loads must have
+// landed, wait_loads() comes first.  The memory clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ void wait_loads() {
     // vmcnt(0); expcnt and lgkmcnt left at their maxima
     __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -457,24 +468,24 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if (j < ntiles) issue_v(j, sV0);
         if (grp == 0) matrix_step(j, sK0, sV1);
         else softmax_step(j - 1);
-        __syncthreads();
+        phase_barrier();
         // phase p+1: leading: softmax(j) ; lagging: matrix(j)
         if (grp == 0) softmax_step(j);
         else matrix_step(j, sK0, sV1);
         wait_loads();
-        __syncthreads();
+        phase_barrier();
         if (p + 2 >= nph) break;
         // phase p+2 (= 2(j+1)): leading: matrix(j+1) ; lagging: softmax(j)
         if (j + 2 < ntiles) issue_k(j + 2, sK0);
         if (j + 1 < ntiles) issue_v(j + 1, sV1);
         if (grp == 0) matrix_step(j + 1, sK1, sV0);
         else softmax_step(j);
-        __syncthreads();
+        phase_barrier();
         // phase p+3: leading: softmax(j+1) ; lagging: matrix(j+1)
         if (grp == 0) softmax_step(j + 1);
         else matrix_step(j + 1, sK1, sV0);
         wait_loads();
-        __syncthreads();
+        phase_barrier();
     }
 
     // ---- epilogue: normalise once, write O (bf16, RNE) and LSE -------------
