@@ -9,12 +9,14 @@ What it computes
 The plain three-step definition of scaled dot-product attention, written out
 in float64 with NumPy:
 
-1. scores      S = scale * Q K^T
+1. scores      S = scale * Q K^T  (+ an ALiBi bias when slopes are given)
    (ops-transformer practice page, jsqmd.com, section 二 "SelfAttention
    baseline and its bottleneck": Attention(Q,K,V) = softmax(QK^T/sqrt(d)) V;
    the naive_attention listing of section 二 "fused computation idea" and the
    BertSelfAttention forward of the agent.csdn.net BERT page, chapter 一,
-   take the same three steps: matmul, softmax, matmul.)
+   take the same three steps: matmul, softmax, matmul.  ALiBi, same page,
+   section 三, the part on ALiBi's linear bias: after QK^T/sqrt(d) every pair
+   (i, j) gets the bias -m * |i - j|, m a slope that depends on the head.)
 2. mask        masked scores are set to -inf, so they vanish after softmax
    (jsqmd.com page, section 二 "causal mask and decode": the upper triangle
    is set to negative infinity; agent.csdn.net BERT page, chapter 四:
@@ -37,6 +39,9 @@ notes):
   ``pos_i = i + Lk - Lq`` and sees keys ``j <= pos_i``;
 * sliding window ``W >= 1`` keeps keys ``j > pos_i - W`` (W keys including
   the diagonal); ``W = -1`` means no window;
+* ALiBi: the page gives no formula for the slopes, so they are an input
+  (one per query head); the distance |i - j| is taken between the query's
+  key position ``pos_i`` (the causal alignment above) and the key index;
 * grouped-query attention maps query head ``h`` to key/value head
   ``h // (Hq // Hkv)`` (contiguous groups); MQA is ``Hkv = 1``;
 * a row with no visible key has O = 0 and LSE = -inf (instead of 0/0);
@@ -82,10 +87,19 @@ def visible_matrix(rows: np.ndarray, Nk: int, Lq: int, Lk: int, causal: bool,
     return vis
 
 
+def alibi_bias(rows: np.ndarray, Nk: int, Lq: int, Lk: int, slope: float) -> np.ndarray:
+    """ALiBi bias ``[len(rows), Nk]``: -slope * |pos_i - j|, pos_i = i + Lk - Lq."""
+    pos = np.asarray(rows, dtype=np.int64)[:, None] + (Lk - Lq)
+    j = np.arange(Nk, dtype=np.int64)[None, :]
+    return -float(slope) * np.abs(pos - j).astype(np.float64)
+
+
 def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                 vis: np.ndarray):
+                 vis: np.ndarray, bias: Optional[np.ndarray] = None):
     """Three-step attention for one (batch, head): q_rows [r, d], k/v [Nk, d]."""
     s = scale * (q_rows @ k.T)                       # step 1
+    if bias is not None:
+        s = s + bias
     s = np.where(vis, s, NEG_INF)                    # step 2
     m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
     # a row is empty only when no key is visible (m = -inf); NaN inputs on
@@ -111,7 +125,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
               seqlens_q: Optional[Sequence[int]] = None,
               seqlens_k: Optional[Sequence[int]] = None,
               rows: Optional[Sequence[int]] = None,
-              heads: Optional[Sequence[int]] = None):
+              heads: Optional[Sequence[int]] = None,
+              alibi_slopes: Optional[Sequence[float]] = None):
     """Reference attention forward.
 
     q: [B, Nq, Hq, d], k and v: [B, Nk, Hkv, d] (any real dtype; used as
@@ -119,7 +134,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     [B, Hq', R] float64, where R = Nq (or ``len(rows)``) and Hq' = Hq (or
     ``len(heads)``).  ``rows`` / ``heads`` restrict the computation to a
     subset of query rows / heads; each output row depends only on its own
-    query and visible keys, so a subset is exact.
+    query and visible keys, so a subset is exact.  ``alibi_slopes`` (one
+    float32 value per query head, or None) adds the ALiBi bias to the scores.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -134,6 +150,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     scale = float(np.float32(scale))
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     heads = np.arange(Hq) if heads is None else np.asarray(heads, dtype=np.int64)
+    if alibi_slopes is not None:
+        slopes = np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
+        if slopes.shape != (Hq,):
+            raise ValueError("alibi_slopes needs one value per query head")
     o = np.zeros((B, len(rows), len(heads), d), dtype=np.float64)
     lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
     for b in range(B):
@@ -142,8 +162,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
         vis = visible_matrix(rows, Nk, Lq, Lk, causal, window_left)
         for hi, h in enumerate(heads):
             kvh = h // group
+            bias = None if alibi_slopes is None else alibi_bias(rows, Nk, Lq, Lk, slopes[h])
             ob, lb = _attend_rows(q[b, rows, h, :], k[b, :, kvh, :], v[b, :, kvh, :],
-                                  scale, vis)
+                                  scale, vis, bias)
             o[b, :, hi, :] = ob
             lse[b, hi, :] = lb
     return o, lse
@@ -151,7 +172,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
 
 def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
            seqlens_k: Sequence[int], *, scale: float, window_left: int = -1,
-           batches: Optional[Sequence[int]] = None):
+           batches: Optional[Sequence[int]] = None,
+           alibi_slopes: Optional[Sequence[float]] = None):
     """Reference single-token decode over a contiguous BSHD cache.
 
     q: [B, Hq, d]; caches: [B, capacity, Hkv, d]; seqlens_k: [B] (clamped to
@@ -170,7 +192,7 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         L = int(min(max(int(seqlens_k[b]), 0), cap))
         ob, lb = attention(q[b][None, None], k_cache[b, :L][None], v_cache[b, :L][None],
                            scale=scale, causal=True, window_left=window_left,
-                           seqlens_q=[1], seqlens_k=[L])
+                           seqlens_q=[1], seqlens_k=[L], alibi_slopes=alibi_slopes)
         o[bi] = ob[0, 0]
         lse[bi] = lb[0, :, 0]
     return o, lse

@@ -432,3 +432,104 @@ def test_nan_on_visible_key_propagates():
     o, lse = oracle.attention(q, k, v, scale=1.0, causal=True)
     assert np.all(o[0, 0, 0] == 1.0) and lse[0, 0, 0] == math.log(1.0)
     assert np.all(np.isnan(o[0, 1:, 0])) and np.all(np.isnan(lse[0, 0, 1:]))
+
+
+# ---------------------------------------------------------------------------
+# ALiBi bias (ops-transformer practice page, section 三: after QK^T/sqrt(d)
+# every pair (i, j) gets -m * |i - j|, m a per-head slope)
+# ---------------------------------------------------------------------------
+def test_alibi_tiny_exact_fractions():
+    """Q = 0 makes every score 0, so with slope ln 2 the weights of row i are
+    2^-|i-j|.  With V the identity (one-hot per key) row i of O is exactly
+    those weights normalised: row 0 of a 4-key non-causal problem is
+    (1, 1/2, 1/4, 1/8) / (15/8) = (8, 4, 2, 1) / 15, row 1 is
+    (1/2, 1, 1/2, 1/4) / (9/4) = (2, 4, 2, 1) / 9."""
+    q = np.zeros((1, 4, 1, 4))
+    k = np.zeros((1, 4, 1, 4))
+    v = np.eye(4)[None, :, None, :]
+    o, lse = oracle.attention(q, k, v, scale=1.0, alibi_slopes=[math.log(2)])
+    ln2 = float(np.float32(math.log(2)))        # slopes pass through float32
+    w = np.exp2(-np.abs(np.arange(4)[:, None] - np.arange(4)[None, :]) * ln2 / math.log(2))
+    np.testing.assert_allclose(o[0, 0, 0], np.array([8, 4, 2, 1]) / 15, rtol=1e-6)
+    np.testing.assert_allclose(o[0, 1, 0], np.array([2, 4, 2, 1]) / 9, rtol=1e-6)
+    np.testing.assert_allclose(o[0, :, 0], w / w.sum(axis=1, keepdims=True), rtol=1e-12)
+    # LSE of row 0 = ln(15/8) up to the float32 rounding of the slope
+    assert abs(lse[0, 0, 0] - math.log(15 / 8)) < 1e-6
+
+
+def test_alibi_causal_geometric_closed_form():
+    """Q = 0, causal, slope m, V = key index: row i averages j <= i with
+    weights r^(i-j), r = e^-m.  With S0 = sum_t r^t and S1 = sum_t t r^t over
+    t = 0..i (geometric series in closed form), O_i = i - S1/S0 and
+    LSE_i = ln S0."""
+    N, m = 50, 0.3
+    q = np.zeros((1, N, 1, 2))
+    k = np.zeros((1, N, 1, 2))
+    v = np.zeros((1, N, 1, 2))
+    v[0, :, 0, 0] = np.arange(N)
+    o, lse = oracle.attention(q, k, v, scale=1.0, causal=True, alibi_slopes=[m])
+    r = math.exp(-float(np.float32(m)))
+    for i in (0, 1, 7, N - 1):
+        S0 = (1 - r ** (i + 1)) / (1 - r)
+        S1 = r * (1 - (i + 1) * r ** i + i * r ** (i + 1)) / (1 - r) ** 2
+        assert abs(o[0, i, 0, 0] - (i - S1 / S0)) < 1e-10
+        assert abs(lse[0, 0, i] - math.log(S0)) < 1e-10
+
+
+def test_alibi_symmetry_and_limits():
+    """Non-causal with Q = 0 and V = key index: the middle row of an odd
+    length sees a symmetric weight profile, so O = its own index.  A huge
+    slope makes each row copy the value of the key at its own position (the
+    only key at distance 0), in both alignments (Lq = Lk and Lq < Lk)."""
+    N = 41
+    q = np.zeros((1, N, 1, 2))
+    k = np.zeros((1, N, 1, 2))
+    v = np.zeros((1, N, 1, 2))
+    v[0, :, 0, 0] = np.arange(N)
+    o, _ = oracle.attention(q, k, v, scale=1.0, alibi_slopes=[0.7])
+    assert abs(o[0, N // 2, 0, 0] - N // 2) < 1e-12
+    rng = np.random.default_rng(3)
+    qr = rng.standard_normal((1, 10, 2, 8))
+    kr = rng.standard_normal((1, 30, 2, 8))
+    vr = rng.standard_normal((1, 30, 2, 8))
+    o, _ = oracle.attention(qr, kr, vr, scale=0.3, causal=True, alibi_slopes=[80.0, 90.0])
+    # query row i sits at key position i + 20 (bottom-right alignment)
+    np.testing.assert_allclose(o[0, :, :, :], vr[0, 20:30], atol=1e-12)
+
+
+def test_alibi_zero_slopes_and_decode_consistency():
+    """Zero slopes change nothing; decode with ALiBi equals the last row of the
+    prefill of the same sequence, whose query sits at position L - 1."""
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((2, 9, 4, 16))
+    k = rng.standard_normal((2, 9, 2, 16))
+    v = rng.standard_normal((2, 9, 2, 16))
+    o0, l0 = oracle.attention(q, k, v, scale=0.25, causal=True)
+    o1, l1 = oracle.attention(q, k, v, scale=0.25, causal=True, alibi_slopes=[0.0] * 4)
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(l0, l1)
+    slopes = [0.5, 0.25, 0.125, 0.0625]
+    op, lp = oracle.attention(q, k, v, scale=0.25, causal=True, alibi_slopes=slopes)
+    od, ld = oracle.decode(q[:, -1], k, v, [9, 9], scale=0.25, alibi_slopes=slopes)
+    np.testing.assert_allclose(od, op[:, -1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ld, lp[:, :, -1], rtol=1e-12, atol=1e-12)
+
+
+def test_alibi_matches_torch_sdpa_float_mask():
+    """Library cross-check: torch's scaled_dot_product_attention (fp64, CPU)
+    with the bias passed as an additive float mask (the causal part as -inf)."""
+    rng = np.random.default_rng(5)
+    B, N, H, d = 2, 33, 3, 16
+    q = rng.standard_normal((B, N, H, d))
+    k = rng.standard_normal((B, N, H, d))
+    v = rng.standard_normal((B, N, H, d))
+    slopes = np.float32([0.3, 0.05, 1.5]).astype(np.float64)
+    o, _ = oracle.attention(q, k, v, scale=d ** -0.5, causal=True, alibi_slopes=slopes)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    bias = -slopes[:, None, None] * np.abs(i - j)[None]
+    bias = np.where(j <= i, bias, -np.inf)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=torch.from_numpy(bias)[None], scale=d ** -0.5)
+    np.testing.assert_allclose(o, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-12)
