@@ -11,6 +11,9 @@ enqueues library calls.  Each call is bracketed by HIP events on the stream
 it is launched on (torch's current stream, which the binding passes to the
 library), so the per-call averages are kernel time plus launch gaps.
 
+After the timed steps, the same two calls are timed with ALiBi slopes
+(reported under "alibi"; not part of the step).
+
 Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
 algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
 decode throughput is reported beside it in GB/s on algorithmic bytes (each
@@ -189,6 +192,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the ALiBi variants of both calls (slopes 2^(-8(h+1)/H)), timed the same way
+    def alibi_slopes(H):
+        return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32,
+                            device=dev)
+    sl_p, sl_d = alibi_slopes(H), alibi_slopes(Hq)
+    n_alibi = max(3, args.steps // 4)
+    fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse, alibi_slopes=sl_p)
+    fa.decode(qd, kc, vc, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws,
+              chunk_keys=args.decode_chunk, alibi_slopes=sl_d)
+    torch.cuda.synchronize()
+    ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_alibi)]
+    for e in ev_a:
+        e[0].record()
+        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse, alibi_slopes=sl_p)
+        e[1].record()
+        fa.decode(qd, kc, vc, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws,
+                  chunk_keys=args.decode_chunk, alibi_slopes=sl_d)
+        e[2].record()
+    torch.cuda.synchronize()
+    pre_a = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_a]))
+    dec_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev_a]))
+
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     flops = prefill_flops(B, H, N, d)
@@ -227,6 +252,11 @@ def main():
                    "ms_median": round(float(np.median(dec_ms)), 4),
                    "ms_min": round(float(dec_ms.min()), 4),
                    "algorithmic_bytes": dbytes},
+        "alibi": {"prefill_ms_mean": round(pre_a, 4),
+                  "prefill_tflops": round(flops / (pre_a * 1e-3) / 1e12, 2),
+                  "decode_ms_mean": round(dec_a, 4),
+                  "decode_gbs": round(dbytes / (dec_a * 1e-3) / 1e9, 1),
+                  "calls": n_alibi},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(["prefill_bf16_kernel<128>"])},

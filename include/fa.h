@@ -88,6 +88,12 @@ typedef enum {
  * written as O = 0, LSE = -inf.  Query head h reads key/value head
  * h / (heads_q / heads_kv) (grouped-query attention; MQA when heads_kv = 1).
  *
+ * ALiBi (jsqmd.com page, section 三, ALiBi's linear bias): when alibi_slopes
+ * is a device fp32 array [heads_q], the score of (i, j) for query head h
+ * becomes softmax_scale * q_i . k_j - alibi_slopes[h] * |i + (Lk - Lq) - j|,
+ * the bias generated in the kernel (no bias matrix in memory).  The slopes
+ * are read on the device, so their values are not validated; NULL = none.
+ *
  * Requirements: head_dim in {64, 128}; heads_q % heads_kv == 0;
  * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
  * window_left == -1 or >= 1; extents >= 0; seqlens arrays (if given) are
@@ -119,6 +125,7 @@ typedef struct {
     int64_t k_stride[3];
     int64_t v_stride[3];
     int64_t o_stride[3];
+    const float *alibi_slopes;           /* device fp32 [heads_q] or NULL        */
 } fa_prefill_params;
 
 /*
@@ -151,6 +158,9 @@ typedef struct {
  * initialisation and are scratch after the call.  Two calls that overlap in
  * time must not share one workspace.
  *
+ * ALiBi: as for prefill, with the query at position L_b - 1: the score of
+ * cache row j for query head h gets - alibi_slopes[h] * (L_b - 1 - j).
+ *
  * Requirements: dtype FA_DTYPE_BF16; head_dim in {64, 128};
  * heads_q % heads_kv == 0; cache_capacity >= 1; softmax_scale finite and > 0.
  */
@@ -175,6 +185,7 @@ typedef struct {
     int64_t k_stride[3];                 /* batch, seq, head                     */
     int64_t v_stride[3];
     int64_t o_stride[2];                 /* batch, head                          */
+    const float *alibi_slopes;           /* device fp32 [heads_q] or NULL        */
 } fa_decode_params;
 
 /* Enqueue the prefill forward pass.  Returns FA_OK, FA_ERR_INVALID_ARG,
@@ -202,7 +213,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10000
+#define FA_ABI_VERSION 10100
 
 #ifdef __cplusplus
 }

@@ -54,11 +54,12 @@ def run_prefill(p, **kw):
     return to_np(o), lse.cpu().numpy().astype(np.float64)
 
 
-def oracle_prefill(p, rows=None, heads=None):
+def oracle_prefill(p, rows=None, heads=None, alibi_slopes=None):
     return oracle.attention(workloads.to_f64(p.q, p.dtype), workloads.to_f64(p.k, p.dtype),
                             workloads.to_f64(p.v, p.dtype), scale=p.scale, causal=p.causal,
                             window_left=p.window_left, seqlens_q=p.seqlens_q,
-                            seqlens_k=p.seqlens_k, rows=rows, heads=heads)
+                            seqlens_k=p.seqlens_k, rows=rows, heads=heads,
+                            alibi_slopes=alibi_slopes)
 
 
 def check(o, lse, ro, rl, dtype, ctx=""):
@@ -102,7 +103,7 @@ def _exact_f32(a, dtype):
     return workloads.bf16_bits_to_f32(a) if dtype == "bf16" else a
 
 
-def oracle_decode(dp, batches=None):
+def oracle_decode(dp, batches=None, alibi_slopes=None):
     return oracle.decode(workloads.to_f64(dp.q, dp.dtype), _exact_f32(dp.k_cache, dp.dtype),
                          _exact_f32(dp.v_cache, dp.dtype), dp.seqlens_k, scale=dp.scale,
-                         window_left=dp.window_left, batches=batches)
+                         window_left=dp.window_left, batches=batches, alibi_slopes=alibi_slopes)

@@ -68,7 +68,7 @@ int main(void) {
   F(fa_prefill_params, seqlens_k) F(fa_prefill_params, q_stride) F(fa_prefill_params, o_stride)
   F(fa_decode_params, softmax_scale) F(fa_decode_params, reserved0) F(fa_decode_params, q)
   F(fa_decode_params, seqlens_k) F(fa_decode_params, q_stride) F(fa_decode_params, k_stride)
-  F(fa_decode_params, o_stride)
+  F(fa_decode_params, o_stride) F(fa_prefill_params, alibi_slopes) F(fa_decode_params, alibi_slopes)
   return 0;
 }
 """

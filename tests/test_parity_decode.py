@@ -131,3 +131,21 @@ def test_no_writes_outside_outputs():
     assert torch.all(l_buf[:pad] == 777.0) and torch.all(l_buf[pad + 24:] == 777.0)
     ro, rl = oracle_decode(dp)
     check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "decode canaries")
+
+
+def test_alibi_decode():
+    """ALiBi on decode: the query sits at L_b - 1, keys get -m_h (L_b - 1 - j)."""
+    dp = workloads.make_decode(58, 6, 16, 4, 128, 3000, (1, 3000), "bf16")
+    slopes = [2.0 ** (-8.0 * (h + 1) / 16) for h in range(16)]
+    say(f"[decode] ALiBi B=6 Hq=16 Hkv=4 cap=3000")
+    o, lse = run_decode(dp, alibi_slopes=slopes)
+    ro, rl = oracle_decode(dp, alibi_slopes=slopes)
+    check(o, lse, ro, rl, dp.dtype, "ALiBi decode")
+
+
+def test_alibi_decode_window_and_d64():
+    dp = workloads.make_decode(59, 5, 8, 2, 64, 1200, (1, 1200), "bf16", window_left=300)
+    slopes = [0.5 * (h + 1) / 8 for h in range(8)]
+    o, lse = run_decode(dp, alibi_slopes=slopes)
+    ro, rl = oracle_decode(dp, alibi_slopes=slopes)
+    check(o, lse, ro, rl, dp.dtype, "ALiBi decode window d64")

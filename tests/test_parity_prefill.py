@@ -260,3 +260,65 @@ def test_rejects_cpu_tensors():
     t = torch.from_numpy(p.q)
     with pytest.raises(ValueError):
         fa.prefill(t, t, t)
+
+
+# ---------------------------------------------------------------------------
+# ALiBi bias (-m_h |pos_i - j| added to the scaled scores)
+# ---------------------------------------------------------------------------
+def _slopes(H, base=8.0):
+    # a geometric sequence of slopes, one per head (any values are valid inputs)
+    return [2.0 ** (-base * (h + 1) / H) for h in range(H)]
+
+
+def _alibi_case(p, slopes, ctx):
+    say(f"[prefill] {ctx} shape(B,Nq,Nk,Hq,Hkv,d)={p.q.shape[0], p.q.shape[1], p.k.shape[1], p.q.shape[2], p.k.shape[2], p.q.shape[3]} "
+        f"causal={p.causal} W={p.window_left} slopes={['%.3g' % s for s in slopes]}")
+    o, lse = run_prefill(p, alibi_slopes=slopes)
+    ro, rl = oracle_prefill(p, alibi_slopes=slopes)
+    check(o, lse, ro, rl, p.dtype, ctx)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_alibi_mha_all_rows(causal):
+    p = workloads.make_prefill(60, 1, 700, 700, 4, 4, 128, "bf16", causal=causal)
+    _alibi_case(p, _slopes(4), f"ALiBi causal={causal}")
+
+
+def test_alibi_gqa_window_lengths_and_offset():
+    """GQA, sliding window and valid lengths with Lq < Lk, so every query's
+    position is shifted by Lk - Lq in both the mask and the bias."""
+    p = workloads.make_prefill(61, 3, 300, 420, 8, 2, 128, "bf16", causal=True, window_left=150)
+    p.seqlens_q = np.array([300, 120, 1], dtype=np.int32)
+    p.seqlens_k = np.array([420, 400, 77], dtype=np.int32)
+    _alibi_case(p, _slopes(8, 4.0), "ALiBi GQA window Lq<Lk")
+
+
+def test_alibi_head_dim_64_and_fp32():
+    _alibi_case(workloads.make_prefill(62, 2, 333, 333, 6, 3, 64, "bf16"), _slopes(6),
+                "ALiBi d64 non-causal")
+    _alibi_case(workloads.make_prefill(63, 2, 200, 200, 4, 2, 128, "f32", causal=True),
+                _slopes(4), "ALiBi fp32 causal")
+
+
+def test_alibi_large_slopes_and_zero_slopes():
+    """Huge slopes concentrate every row on its own key position (O -> V_pos);
+    zero slopes give bit-identical results to no ALiBi at all."""
+    p = workloads.make_prefill(64, 1, 260, 260, 2, 2, 128, "bf16", causal=True)
+    _alibi_case(p, [50.0, 200.0], "ALiBi huge slopes")
+    q, k, v, sq, sk = prefill_inputs(p)
+    o0, l0 = fa.prefill(q, k, v, causal=True, scale=p.scale)
+    o1, l1 = fa.prefill(q, k, v, causal=True, scale=p.scale, alibi_slopes=[0.0, 0.0])
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_alibi_causal_8k_sampled():
+    """Full-size causal N=8192 with ALiBi, sampled rows and heads."""
+    p = workloads.make_workload(3)
+    slopes = _slopes(p.q.shape[2])
+    rows = np.array([0, 1, 63, 64, 255, 256, 4095, 4096, 8000, 8191])
+    heads = np.array([0, 7, 31])
+    say(f"[prefill] ALiBi causal 8k sampled rows={rows.tolist()} heads={heads.tolist()}")
+    o, lse = run_prefill(p, alibi_slopes=slopes)
+    ro, rl = oracle_prefill(p, rows=rows, heads=heads, alibi_slopes=slopes)
+    check(o[:, rows][:, :, heads], lse[:, heads][:, :, rows], ro, rl, p.dtype, "ALiBi 8k sampled")

@@ -68,9 +68,21 @@ def _seqlens(x, B, device):
     return x
 
 
+def _slopes(x, H, device):
+    torch = _torch()
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        x = torch.tensor(list(x), dtype=torch.float32)
+    x = x.to(device=device, dtype=torch.float32).contiguous()
+    if x.numel() != H:
+        raise ValueError(f"alibi_slopes must have {H} entries (one per query head)")
+    return x
+
+
 def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[float] = None,
-            seqlens_q=None, seqlens_k=None, out=None, lse=None, return_lse: bool = True
-            ) -> Tuple[object, object]:
+            seqlens_q=None, seqlens_k=None, out=None, lse=None, return_lse: bool = True,
+            alibi_slopes=None) -> Tuple[object, object]:
     """Fused attention forward for a batch of sequences.
 
     q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (any strides with a unit last
@@ -79,6 +91,8 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     ``return_lse`` is False.  ``window`` keeps the last ``window`` keys up to
     and including the diagonal; ``seqlens_q`` / ``seqlens_k`` are per-sequence
     valid lengths (rows past ``seqlens_q`` come back as O = 0, LSE = -inf).
+    ``alibi_slopes`` (one value per query head) adds the ALiBi bias
+    -slope_h * |pos_i - j| to the scaled scores, pos_i = i + Lk - Lq.
     """
     torch = _torch()
     _require_gpu(q, k, v)
@@ -100,6 +114,7 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
     sq = _seqlens(seqlens_q, B, dev)
     sk = _seqlens(seqlens_k, B, dev)
+    al = _slopes(alibi_slopes, Hq, dev)
     p = _lib.PrefillParams()
     p.dtype = _dtype_code(q)
     p.batch, p.seqlen_q, p.seqlen_k = B, Nq, Nk
@@ -115,11 +130,12 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     p.k_stride[:] = [k.stride(0), k.stride(1), k.stride(2)]
     p.v_stride[:] = [v.stride(0), v.stride(1), v.stride(2)]
     p.o_stride[:] = [out.stride(0), out.stride(1), out.stride(2)]
+    p.alibi_slopes = al.data_ptr() if al is not None else None
     _lib.check(_lib.prefill_fwd(p, _stream(dev)), "fa_prefill_fwd")
     return out, (lse if return_lse else None)
 
 
-def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys):
+def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys, al=None):
     B, Hq, d = q.shape
     _, cap, Hkv, _ = k_cache.shape
     p = _lib.DecodeParams()
@@ -140,6 +156,7 @@ def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys)
     p.v_stride[:] = [v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)]
     if out is not None:
         p.o_stride[:] = [out.stride(0), out.stride(1)]
+    p.alibi_slopes = al.data_ptr() if al is not None else None
     return p
 
 
@@ -153,14 +170,16 @@ def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
 
 
 def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, window: int = -1,
-           chunk_keys: int = 0, workspace=None, out=None, lse=None, return_lse: bool = True):
+           chunk_keys: int = 0, workspace=None, out=None, lse=None, return_lse: bool = True,
+           alibi_slopes=None):
     """Single-token decode over a contiguous KV cache.
 
     q: [B, Hq, d]; k_cache, v_cache: [B, capacity, Hkv, d]; seqlens_k: [B]
     valid lengths (the current token already appended).  Returns ``(o, lse)``:
     o [B, Hq, d] like q, lse fp32 [B, Hq].  ``workspace`` (a uint8 GPU tensor
     of at least ``decode_workspace_size`` bytes) may be passed to avoid an
-    allocation per call.
+    allocation per call.  ``alibi_slopes`` (one value per query head) adds the
+    ALiBi bias -slope_h * (L_b - 1 - j).
     """
     torch = _torch()
     _require_gpu(q, k_cache, v_cache)
@@ -180,8 +199,9 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
         out = torch.empty((B, Hq, d), dtype=q.dtype, device=dev)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    al = _slopes(alibi_slopes, Hq, dev)
     p = _decode_params(q, k_cache, v_cache, sk, out, lse if return_lse else None, scale, window,
-                       chunk_keys)
+                       chunk_keys, al)
     st, need = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     if workspace is None:

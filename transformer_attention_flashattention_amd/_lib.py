@@ -54,6 +54,7 @@ class PrefillParams(ctypes.Structure):
         ("k_stride", _i64x3),
         ("v_stride", _i64x3),
         ("o_stride", _i64x3),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 
@@ -79,6 +80,7 @@ class DecodeParams(ctypes.Structure):
         ("k_stride", _i64x3),
         ("v_stride", _i64x3),
         ("o_stride", _i64x2),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 

@@ -133,8 +133,9 @@ __device__ __forceinline__ u32x4 load_nt(const char *base, unsigned off) {
 }
 
 // D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
-// a slice of it).  Chunk lengths are multiples of NWAVES * KT.
-template <int D, int GT>
+// a slice of it); ALIBI: add the per-head linear bias -m (L - 1 - j).  Chunk
+// lengths are multiples of NWAVES * KT.
+template <int D, int GT, bool ALIBI>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
     constexpr int SKP = 64 / SL;             // keys per score pass
@@ -234,6 +235,10 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
     }
     const float c2 = a.scale_log2;
+    // ALiBi in raw score units (see the prefill kernel): s - (m / scale) (L - 1 - j)
+    float alibi_raw[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) alibi_raw[g] = ALIBI ? -a.alibi[h0 + g] / a.scale : 0.f;
 
     // This wavefront's tiles t = 0 .. C/128 - 1 start at key base + 128 t; the
     // ones holding a visible key form one contiguous range [ta, tb).
@@ -280,6 +285,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc = dot2(kt[p][1][i], qr[g][4 + i], acc);
                 acc = group_sum<SL>(acc);
+                if constexpr (ALIBI) acc = __builtin_fmaf((float)(L - 1 - j), alibi_raw[g], acc);
                 s[p][g] = ok ? acc : -INFINITY;
             }
         }
@@ -502,7 +508,8 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
 template <int D, int GT>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)(a.heads_kv * a.head_groups) * a.batch * a.max_chunks);
-    hipLaunchKernelGGL((decode_split_kernel<D, GT>), grid, dim3(NTHREADS), 0, s, a);
+    if (a.alibi) hipLaunchKernelGGL((decode_split_kernel<D, GT, true>), grid, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, GT, false>), grid, dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 

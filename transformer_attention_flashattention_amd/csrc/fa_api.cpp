@@ -189,6 +189,7 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     a.causal = p->causal; a.window_left = p->window_left;
     a.scale = p->softmax_scale;
     a.scale_log2 = p->softmax_scale * kLog2e;
+    a.alibi = p->alibi_slopes;
     const int bm = p->dtype == FA_DTYPE_BF16 ? fa::kPrefillBM : fa::kPrefillF32BM;
     a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
     if ((int64_t)a.num_q_tiles * a.heads_q * a.batch > 0x7fffffffLL)
@@ -241,6 +242,8 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     a.capacity = p->cache_capacity; a.window_left = p->window_left;
     a.chunk = chunk; a.max_chunks = max_chunks; a.head_groups = group / gt;
     a.scale_log2 = p->softmax_scale * kLog2e;
+    a.scale = p->softmax_scale;
+    a.alibi = p->alibi_slopes;
     const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
     const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = static_cast<float *>(workspace);

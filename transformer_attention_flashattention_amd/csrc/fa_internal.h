@@ -24,6 +24,7 @@ struct PrefillArgs {
     float scale_log2;              // softmax_scale * log2(e)
     float scale;                   // softmax_scale
     int32_t num_q_tiles;
+    const float *alibi;            // ALiBi slopes [heads_q] or null
 };
 
 struct DecodeArgs {
@@ -42,6 +43,8 @@ struct DecodeArgs {
     float scale_log2;
     float *ws_o;                   // [batch, heads_q, max_chunks, head_dim] fp32
     float *ws_ml;                  // [batch, heads_q, max_chunks, 2] fp32 (m, l)
+    const float *alibi;            // ALiBi slopes [heads_q] or null
+    float scale;                   // softmax_scale
 };
 
 // Each launcher enqueues its kernel(s) and returns the launch status.

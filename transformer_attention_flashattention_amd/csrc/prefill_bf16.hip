@@ -171,7 +171,8 @@ __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
                  : "memory", "m0");
 }
 
-template <int D>
+// D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores.
+template <int D, bool ALIBI>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
@@ -324,6 +325,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const float c2 = a.scale_log2;
     const int vis_hi = a.causal ? min(Lk, pos + 1) : Lk;
     const int vis_lo = (W > 0) ? pos - W + 1 : INT_MIN;
+    // ALiBi in raw score units (the accumulators hold q.k; the exponent is
+    // scale_log2 * s): scale * s - m |pos - j| = scale * (s - (m / scale) |pos - j|)
+    float alibi_raw = 0.f;
+    if constexpr (ALIBI) alibi_raw = -a.alibi[h] / a.scale;
 
     // matrix step of tile j: PV of tile j-1 (from vb), then S of tile j (from kb).
     // Operand reads are issued in the order the MFMAs consume them and the
@@ -394,6 +399,17 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const bool need_mask = (k0 + BN > Lk) ||
                                (a.causal && k0 + BN - 1 > q0w + offset) ||
                                (W > 0 && k0 <= q0w + 31 + offset - W);
+        if constexpr (ALIBI) {
+            // distance |pos - key| with key = k0 + half*8 + sb*32 + 16*(r/8) + r%8
+            const float base = (float)(pos - k0 - half * 8);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float dist = fabsf(base - (float)(sb * 32 + ((r >> 3) << 4) + (r & 7)));
+                    s[sb][r] = __builtin_fmaf(dist, alibi_raw, s[sb][r]);
+                }
+        }
         if (need_mask) {
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
@@ -516,10 +532,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)a.num_q_tiles * a.heads_q * a.batch);
     const dim3 block(NTHREADS);
-    if (head_dim == 128)
-        hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, s, a);
+    const bool alibi = a.alibi != nullptr;
+    if (head_dim == 128) {
+        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+    } else {
+        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -71,6 +71,8 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
     for (int d = 0; d < D; ++d) o[d] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
     const float c2 = a.scale_log2;
+    // ALiBi in raw score units: scale * s + bias = scale * (s + bias / scale)
+    const float alibi_raw = a.alibi ? -a.alibi[h] / a.scale : 0.f;
 
     for (int t = t_begin; t < t_end; ++t) {
         const int k0 = t * BN;
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
             bool vis = key < Lk;
             if (a.causal) vis = vis && key <= pos;
             if (W > 0) vis = vis && key > pos - W;
+            if (a.alibi) s[j] = __builtin_fmaf(fabsf((float)(pos - key)), alibi_raw, s[j]);
             s[j] = vis ? s[j] : -INFINITY;
             mx = fmaxf(mx, s[j]);
         }
