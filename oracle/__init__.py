@@ -5,4 +5,5 @@ leg may import anything under ``oracle/``.  The library's product path
 (the C ABI in ``include/fa.h`` and its Python binding) never calls it, and
 the two share no code.
 """
-from .attention import alibi_bias, attention, decode, visible, visible_matrix  # noqa: F401
+from .attention import (alibi_bias, attention, decode, decode_paged, gather_paged,  # noqa: F401
+                        visible, visible_matrix)

@@ -47,7 +47,17 @@ notes):
 * a row with no visible key has O = 0 and LSE = -inf (instead of 0/0);
 * decode (the BERT page's closing section: the new token attends to all
   cached keys, the cache is not recomputed) is the same computation with a
-  single query at position ``L_b - 1`` over cache rows ``0 .. L_b - 1``.
+  single query at position ``L_b - 1`` over cache rows ``0 .. L_b - 1``;
+* paged KV cache (GatherPAKVCache, the hwcomputing.csdn.net page, sections
+  1.2 and 4.1: the cache rows a query needs are gathered by index rather
+  than read as one contiguous block).  The page does not define the index
+  structure; the reading here is the paged layout: a pool of pages of
+  ``page_size`` consecutive rows each, and per sequence a table whose entry
+  ``p`` names the physical page that holds logical rows
+  ``p * page_size .. (p + 1) * page_size - 1``.  The attention computed over
+  the gathered rows is the decode above, unchanged.  The page's other
+  strategies (keeping only "important" rows) change the result and have no
+  stated criterion; they are not part of this oracle.
 
 Every function here is pinned in ``tests/test_oracle.py`` against closed
 forms, brute force on tiny integer inputs, library routines and invariants.
@@ -193,6 +203,50 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         ob, lb = attention(q[b][None, None], k_cache[b, :L][None], v_cache[b, :L][None],
                            scale=scale, causal=True, window_left=window_left,
                            seqlens_q=[1], seqlens_k=[L], alibi_slopes=alibi_slopes)
+        o[bi] = ob[0, 0]
+        lse[bi] = lb[0, :, 0]
+    return o, lse
+
+
+def gather_paged(pool: np.ndarray, table_row: Sequence[int], L: int) -> np.ndarray:
+    """Logical rows ``0 .. L - 1`` of one sequence from a paged pool.
+
+    pool: [num_pages, page_size, ...]; row j is slot ``j % page_size`` of
+    physical page ``table_row[j // page_size]``.
+    """
+    P = pool.shape[1]
+    rows = [pool[int(table_row[j // P]), j % P] for j in range(L)]
+    if not rows:
+        return np.zeros((0,) + pool.shape[2:], dtype=pool.dtype)
+    return np.stack(rows)
+
+
+def decode_paged(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                 block_table: np.ndarray, seqlens_k: Sequence[int], *, scale: float,
+                 window_left: int = -1, batches: Optional[Sequence[int]] = None,
+                 alibi_slopes: Optional[Sequence[float]] = None):
+    """Reference single-token decode over a paged KV cache.
+
+    q: [B, Hq, d]; pools: [num_pages, page_size, Hkv, d]; block_table:
+    [B, pages_per_seq] physical page numbers.  The logical capacity is
+    ``pages_per_seq * page_size``; lengths are clamped to [0, capacity].  The
+    rows of sequence b are gathered by the table and attended exactly as
+    :func:`decode` does for a contiguous cache.  Returns O: [B', Hq, d] and
+    LSE: [B', Hq] in float64.
+    """
+    B, Hq, d = q.shape
+    block_table = np.asarray(block_table)
+    cap = block_table.shape[1] * k_pool.shape[1]
+    batches = list(range(B) if batches is None else batches)
+    o = np.zeros((len(batches), Hq, d), dtype=np.float64)
+    lse = np.zeros((len(batches), Hq), dtype=np.float64)
+    for bi, b in enumerate(batches):
+        L = int(min(max(int(seqlens_k[b]), 0), cap))
+        kb = gather_paged(k_pool, block_table[b], L)
+        vb = gather_paged(v_pool, block_table[b], L)
+        ob, lb = attention(q[b][None, None], kb[None], vb[None], scale=scale, causal=True,
+                           window_left=window_left, seqlens_q=[1], seqlens_k=[L],
+                           alibi_slopes=alibi_slopes)
         o[bi] = ob[0, 0]
         lse[bi] = lb[0, :, 0]
     return o, lse

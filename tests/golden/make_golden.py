@@ -20,6 +20,8 @@ def main():
         "prefill_small": workloads.make_prefill(5, 2, 70, 70, 4, 2, 64, "bf16", causal=True,
                                                 seqlens_k_range=(1, 70)).sha256(),
         "decode_small": workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16").sha256(),
+        "decode_paged_small": workloads.make_decode_paged(6, 3, 4, 2, 64, 300, (1, 300), 16,
+                                                          "bf16").sha256(),
     }
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "input_hashes.json")
     with open(path, "w") as f:

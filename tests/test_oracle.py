@@ -421,6 +421,8 @@ def test_generator_hashes_are_stable():
     assert small.sha256() == stored["prefill_small"]
     dec = workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16")
     assert dec.sha256() == stored["decode_small"]
+    pdec = workloads.make_decode_paged(6, 3, 4, 2, 64, 300, (1, 300), 16, "bf16")
+    assert pdec.sha256() == stored["decode_paged_small"]
 
 
 def test_nan_on_visible_key_propagates():
@@ -533,3 +535,89 @@ def test_alibi_matches_torch_sdpa_float_mask():
     ref = torch.nn.functional.scaled_dot_product_attention(
         t(q), t(k), t(v), attn_mask=torch.from_numpy(bias)[None], scale=d ** -0.5)
     np.testing.assert_allclose(o, ref.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache: the gather and decode over it
+# ---------------------------------------------------------------------------
+def test_gather_paged_literal():
+    """Page p, slot s of this pool holds 2p + s; the rows are read off by hand."""
+    pool = np.arange(8).reshape(4, 2)
+    assert oracle.gather_paged(pool, [2, 0, 3], 5).tolist() == [4, 5, 0, 1, 6]
+    assert oracle.gather_paged(pool, [3, 1], 4).tolist() == [6, 7, 2, 3]
+    assert oracle.gather_paged(pool, [1], 0).shape == (0,)
+
+
+def _scatter_pages(cache, lengths, P, seed):
+    """Inverse of the gather, written independently of the oracle: each
+    sequence's rows go page by page into shuffled physical pages; unused
+    slots, the spare page and every table entry past the used pages are NaN."""
+    B, cap = cache.shape[:2]
+    per = -(-cap // P)
+    used = [-(-int(L) // P) for L in lengths]
+    n_pages = sum(used) + 1
+    order = np.random.default_rng(seed).permutation(n_pages)
+    pool = np.full((n_pages, P) + cache.shape[2:], np.nan)
+    table = np.full((B, per), order[-1], dtype=np.int64)
+    nxt = 0
+    for b in range(B):
+        for pg in range(used[b]):
+            phys = order[nxt]
+            nxt += 1
+            table[b, pg] = phys
+            rows = cache[b, pg * P:min(int(lengths[b]), (pg + 1) * P)]
+            pool[phys, :len(rows)] = rows
+    return pool, table
+
+
+@pytest.mark.parametrize("P", [1, 3, 16])
+@pytest.mark.parametrize("window", [-1, 5])
+def test_paged_decode_equals_contiguous(P, window):
+    """Same logical rows in a shuffled pool: the same result, bit for bit."""
+    prob = workloads.make_decode(43, 4, 8, 2, 16, 96, (0, 96), "bf16",
+                                 lengths=np.array([1, 17, 96, 0], dtype=np.int32))
+    q = workloads.to_f64(prob.q, "bf16")
+    kc = workloads.to_f64(prob.k_cache, "bf16")
+    vc = workloads.to_f64(prob.v_cache, "bf16")
+    slopes = np.linspace(0.05, 0.4, 8).astype(np.float32)
+    kp, table = _scatter_pages(kc, prob.seqlens_k, P, seed=P)
+    vp, table2 = _scatter_pages(vc, prob.seqlens_k, P, seed=P)
+    assert np.array_equal(table, table2)
+    for sl in (None, slopes):
+        o_ref, l_ref = oracle.decode(q, kc, vc, prob.seqlens_k, scale=prob.scale,
+                                     window_left=window, alibi_slopes=sl)
+        o, l = oracle.decode_paged(q, kp, vp, table, prob.seqlens_k, scale=prob.scale,
+                                   window_left=window, alibi_slopes=sl)
+        assert np.array_equal(o, o_ref) and np.array_equal(l, l_ref)
+        assert np.isfinite(o).all()
+
+
+def test_paged_decode_zero_query_mean_of_gathered_rows():
+    """q = 0: O is the mean of the gathered V rows, LSE = ln L (hand-checked rows)."""
+    vp = np.zeros((3, 2, 1, 1))
+    vp[:, :, 0, 0] = [[1.0, 2.0], [10.0, 20.0], [100.0, 200.0]]
+    kp = np.ones_like(vp)
+    q = np.zeros((1, 1, 1))
+    table = np.array([[2, 0]])
+    o, l = oracle.decode_paged(q, kp, vp, table, [3], scale=1.0)
+    assert o[0, 0, 0] == pytest.approx((100.0 + 200.0 + 1.0) / 3, abs=1e-12)
+    assert l[0, 0] == pytest.approx(math.log(3), abs=1e-12)
+    # lengths clamp to the table's capacity (2 pages x 2 slots)
+    o, l = oracle.decode_paged(q, kp, vp, table, [9], scale=1.0)
+    assert o[0, 0, 0] == pytest.approx((100.0 + 200.0 + 1.0 + 2.0) / 4, abs=1e-12)
+
+
+def test_paged_generator_holds_the_contiguous_rows():
+    """The paged generator and the contiguous one hold the same logical cache."""
+    a = workloads.make_decode(44, 3, 4, 2, 8, 100, (1, 100), "bf16")
+    p = workloads.make_decode_paged(44, 3, 4, 2, 8, 100, (1, 100), 16, "bf16")
+    assert np.array_equal(a.q, p.q) and np.array_equal(a.seqlens_k, p.seqlens_k)
+    for b in range(3):
+        L = int(a.seqlens_k[b])
+        assert np.array_equal(oracle.gather_paged(p.k_pool, p.block_table[b], L), a.k_cache[b, :L])
+        assert np.array_equal(oracle.gather_paged(p.v_pool, p.block_table[b], L), a.v_cache[b, :L])
+    # every table entry past the used pages names a NaN page
+    for b in range(3):
+        used = -(-int(p.seqlens_k[b]) // 16)
+        for e in p.block_table[b, used:]:
+            assert (p.k_pool[e] == workloads.BF16_QNAN).all()

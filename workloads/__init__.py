@@ -185,6 +185,88 @@ def make_decode(seed: int, B: int, Hq: int, Hkv: int, d: int, capacity: int,
     return DecodeProblem(dtype, _store(q, dtype), kc, vc, lengths, scale, window_left)
 
 
+@dataclasses.dataclass
+class PagedDecodeProblem:
+    dtype: str
+    q: np.ndarray                    # [B, Hq, d]
+    k_pool: np.ndarray               # [num_pages, page_size, Hkv, d]
+    v_pool: np.ndarray               # [num_pages, page_size, Hkv, d]
+    block_table: np.ndarray          # int32 [B, pages_per_seq]
+    seqlens_k: np.ndarray            # int32 [B]
+    scale: float
+    window_left: int = -1
+
+    @property
+    def page_size(self) -> int:
+        return self.k_pool.shape[1]
+
+    def sha256(self) -> str:
+        h = hashlib.sha256()
+        for a in (self.q, self.k_pool, self.v_pool, self.block_table, self.seqlens_k):
+            h.update(np.ascontiguousarray(a).tobytes())
+        return h.hexdigest()
+
+    @property
+    def capacity(self) -> int:
+        return self.block_table.shape[1] * self.page_size
+
+
+def make_decode_paged(seed: int, B: int, Hq: int, Hkv: int, d: int, capacity: int,
+                      len_range: tuple, page_size: int, dtype: str = "bf16", *,
+                      scale: Optional[float] = None, window_left: int = -1,
+                      lengths: Optional[np.ndarray] = None,
+                      spare_pages: int = 1) -> PagedDecodeProblem:
+    """Draw a single-token decode problem over a paged KV cache.
+
+    The draws are those of :func:`make_decode` with the same arguments
+    (lengths, Q, then per sequence its K rows and V rows), so both layouts hold
+    the same logical cache for one seed.  Each sequence's rows then go, page by
+    page in logical order, into physical pages taken from a seeded random
+    permutation of the pool (a fragmented pool).  ``pages_per_seq`` is
+    ``ceil(capacity / page_size)``.  The pool holds the pages in use plus
+    ``spare_pages`` (>= 1) pages of NaN; slots past a sequence's length in its
+    last page hold NaN, and every table entry past the pages in use names the
+    first spare page, so any read the lengths do not allow poisons the output.
+    """
+    if spare_pages < 1:
+        raise ValueError("spare_pages must be >= 1")
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lo, hi = len_range
+        lengths = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    q = rng.standard_normal((B, Hq, d), dtype=np.float32)
+    P = int(page_size)
+    per_seq = -(-capacity // P)
+    used = [-(-int(min(max(L, 0), capacity)) // P) for L in lengths]
+    n_pages = sum(used) + spare_pages
+    fill = BF16_QNAN if dtype == "bf16" else np.float32(np.nan)
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    kp = np.full((n_pages, P, Hkv, d), fill, dtype=sdt)
+    vp = np.full((n_pages, P, Hkv, d), fill, dtype=sdt)
+    rows_k, rows_v = [], []
+    for b in range(B):
+        L = int(min(max(lengths[b], 0), capacity))
+        rows_k.append(_store(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype))
+        rows_v.append(_store(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype))
+    order = rng.permutation(n_pages).astype(np.int32)
+    spare = order[sum(used)]
+    table = np.full((B, per_seq), spare, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        L = rows_k[b].shape[0]
+        for pg in range(used[b]):
+            phys = order[nxt]
+            nxt += 1
+            table[b, pg] = phys
+            n = min(P, L - pg * P)
+            kp[phys, :n] = rows_k[b][pg * P:pg * P + n]
+            vp[phys, :n] = rows_v[b][pg * P:pg * P + n]
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(d)))
+    return PagedDecodeProblem(dtype, _store(q, dtype), kp, vp, table, lengths, scale, window_left)
+
+
 # --------------------------------------------------------------------------
 # The five named workloads
 # --------------------------------------------------------------------------
