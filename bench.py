@@ -12,7 +12,9 @@ it is launched on (torch's current stream, which the binding passes to the
 library), so the per-call averages are kernel time plus launch gaps.
 
 After the timed steps, the same two calls are timed with ALiBi slopes
-(reported under "alibi"; not part of the step).
+(reported under "alibi"), and the decode call over the same logical cache
+held in a paged pool of 16-row pages in shuffled order (reported under
+"paged"); neither is part of the step.
 
 Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
 algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
@@ -214,6 +216,25 @@ def main():
     pre_a = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_a]))
     dec_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev_a]))
 
+    # the decode over a paged pool holding the same logical cache
+    page = 16
+    pp = workloads.make_workload_paged(5, page)
+    assert np.array_equal(pp.seqlens_k, dp.seqlens_k)
+    qp, kp, vp = (to_dev(x, "bf16", torch, dev) for x in (pp.q, pp.k_pool, pp.v_pool))
+    tab = torch.from_numpy(pp.block_table).to(dev)
+    fa.decode(qp, kp, vp, sk, scale=pp.scale, out=od, lse=lsed, workspace=ws,
+              chunk_keys=args.decode_chunk, block_table=tab)
+    torch.cuda.synchronize()
+    ev_p = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_alibi)]
+    for e in ev_p:
+        e[0].record()
+        fa.decode(qp, kp, vp, sk, scale=pp.scale, out=od, lse=lsed, workspace=ws,
+                  chunk_keys=args.decode_chunk, block_table=tab)
+        e[1].record()
+    torch.cuda.synchronize()
+    dec_p = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_p]))
+    table_bytes = 4 * int(sum(-(-int(L) // page) for L in pp.seqlens_k))
+
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
     flops = prefill_flops(B, H, N, d)
@@ -256,6 +277,10 @@ def main():
                   "prefill_tflops": round(flops / (pre_a * 1e-3) / 1e12, 2),
                   "decode_ms_mean": round(dec_a, 4),
                   "decode_gbs": round(dbytes / (dec_a * 1e-3) / 1e9, 1),
+                  "calls": n_alibi},
+        "paged": {"page_size": page, "num_pages": int(pp.k_pool.shape[0]),
+                  "decode_ms_mean": round(dec_p, 4),
+                  "decode_gbs": round((dbytes + table_bytes) / (dec_p * 1e-3) / 1e9, 1),
                   "calls": n_alibi},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

@@ -161,6 +161,22 @@ typedef struct {
  * ALiBi: as for prefill, with the query at position L_b - 1: the score of
  * cache row j for query head h gets - alibi_slopes[h] * (L_b - 1 - j).
  *
+ * Paged KV cache (block_table != NULL): the gather-by-index cache of the
+ * hwcomputing.csdn.net page (GatherPAKVCache, sections 1.2 and 4.1), in the
+ * paged layout.  k_cache and v_cache are then pools of num_pages pages of
+ * page_size rows each, [num_pages, page_size, heads_kv, head_dim] via
+ * k_stride / v_stride (page, row, head), and block_table is a device int32
+ * array [batch, pages_per_seq]: logical row j of sequence b is row
+ * j % page_size of physical page block_table[b * pages_per_seq + j / page_size].
+ * The caller owns the pools and the table.  Only the entries of pages that
+ * hold rows the query reads are loaded; an entry outside [0, num_pages) is
+ * clamped into that range (no read leaves the pools, but that sequence's
+ * result is then meaningless).  Requirements: page_size a multiple of 16 in
+ * [16, 65536]; pages_per_seq >= 1; num_pages >= 1; cache_capacity <=
+ * pages_per_seq * page_size (lengths clamp to cache_capacity); page_size
+ * times the row stride of k and v below 2^31 elements.  With block_table
+ * NULL, page_size, pages_per_seq and num_pages must be 0.
+ *
  * Requirements: dtype FA_DTYPE_BF16; head_dim in {64, 128};
  * heads_q % heads_kv == 0; cache_capacity >= 1; softmax_scale finite and > 0.
  */
@@ -186,6 +202,11 @@ typedef struct {
     int64_t v_stride[3];
     int64_t o_stride[2];                 /* batch, head                          */
     const float *alibi_slopes;           /* device fp32 [heads_q] or NULL        */
+    const int32_t *block_table;          /* device [batch, pages_per_seq] or NULL */
+    int32_t page_size;                   /* rows per page (paged cache), else 0  */
+    int32_t pages_per_seq;               /* block_table row length, else 0       */
+    int32_t num_pages;                   /* pages in each pool, else 0           */
+    int32_t reserved1;                   /* must be 0                            */
 } fa_decode_params;
 
 /* Enqueue the prefill forward pass.  Returns FA_OK, FA_ERR_INVALID_ARG,
@@ -213,7 +234,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10100
+#define FA_ABI_VERSION 10200
 
 #ifdef __cplusplus
 }

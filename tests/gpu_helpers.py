@@ -107,3 +107,28 @@ def oracle_decode(dp, batches=None, alibi_slopes=None):
     return oracle.decode(workloads.to_f64(dp.q, dp.dtype), _exact_f32(dp.k_cache, dp.dtype),
                          _exact_f32(dp.v_cache, dp.dtype), dp.seqlens_k, scale=dp.scale,
                          window_left=dp.window_left, batches=batches, alibi_slopes=alibi_slopes)
+
+
+def paged_inputs(pp):
+    q, kp, vp = (dev_tensor(x, pp.dtype) for x in (pp.q, pp.k_pool, pp.v_pool))
+    sk = torch.from_numpy(pp.seqlens_k).to(DEV)
+    table = torch.from_numpy(pp.block_table).to(DEV)
+    return q, kp, vp, sk, table
+
+
+def run_decode_paged(pp, **kw):
+    q, kp, vp, sk, table = paged_inputs(pp)
+    o, lse = fa.decode(q, kp, vp, sk, scale=pp.scale, window=pp.window_left, block_table=table,
+                       **kw)
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_decode_paged(pp, batches=None, alibi_slopes=None, capacity=None):
+    seqlens = pp.seqlens_k
+    if capacity is not None:
+        seqlens = np.minimum(seqlens, capacity)
+    return oracle.decode_paged(workloads.to_f64(pp.q, pp.dtype), _exact_f32(pp.k_pool, pp.dtype),
+                               _exact_f32(pp.v_pool, pp.dtype), pp.block_table, seqlens,
+                               scale=pp.scale, window_left=pp.window_left, batches=batches,
+                               alibi_slopes=alibi_slopes)

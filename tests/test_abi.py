@@ -69,6 +69,8 @@ int main(void) {
   F(fa_decode_params, softmax_scale) F(fa_decode_params, reserved0) F(fa_decode_params, q)
   F(fa_decode_params, seqlens_k) F(fa_decode_params, q_stride) F(fa_decode_params, k_stride)
   F(fa_decode_params, o_stride) F(fa_prefill_params, alibi_slopes) F(fa_decode_params, alibi_slopes)
+  F(fa_decode_params, block_table) F(fa_decode_params, page_size) F(fa_decode_params, pages_per_seq)
+  F(fa_decode_params, num_pages) F(fa_decode_params, reserved1)
   return 0;
 }
 """
@@ -199,6 +201,24 @@ def _decode(**kw):
     (dict(chunk_keys=-128), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
     (dict(chunk_keys=65536 + 128), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
     (dict(reserved0=1), _lib.FA_ERR_INVALID_ARG, "reserved0"),
+    (dict(reserved1=1), _lib.FA_ERR_INVALID_ARG, "reserved1"),
+    # paged-cache fields without a table, and bad paged parameters
+    (dict(page_size=16), _lib.FA_ERR_INVALID_ARG, "without a block_table"),
+    (dict(num_pages=4), _lib.FA_ERR_INVALID_ARG, "without a block_table"),
+    (dict(block_table=FAKE + 24576, page_size=8, pages_per_seq=1024, num_pages=100),
+     _lib.FA_ERR_UNSUPPORTED, "page_size"),
+    (dict(block_table=FAKE + 24576, page_size=24, pages_per_seq=512, num_pages=100),
+     _lib.FA_ERR_UNSUPPORTED, "page_size"),
+    (dict(block_table=FAKE + 24576, page_size=65536 + 16, pages_per_seq=1, num_pages=100),
+     _lib.FA_ERR_UNSUPPORTED, "page_size"),
+    (dict(block_table=FAKE + 24576, page_size=16, pages_per_seq=0, num_pages=100),
+     _lib.FA_ERR_INVALID_ARG, "pages_per_seq"),
+    (dict(block_table=FAKE + 24576, page_size=16, pages_per_seq=512, num_pages=0),
+     _lib.FA_ERR_INVALID_ARG, "num_pages"),
+    (dict(block_table=FAKE + 24576, page_size=16, pages_per_seq=511, num_pages=100),
+     _lib.FA_ERR_INVALID_ARG, "exceeds pages_per_seq"),
+    (dict(block_table=FAKE + 24578, page_size=16, pages_per_seq=512, num_pages=100),
+     _lib.FA_ERR_INVALID_ARG, "4-byte"),
     (dict(softmax_scale=float("inf")), _lib.FA_ERR_INVALID_ARG, "softmax_scale"),
     (dict(seqlens_k=None), _lib.FA_ERR_INVALID_ARG, "seqlens_k"),
     (dict(k_cache=FAKE + 8), _lib.FA_ERR_UNSUPPORTED, "aligned"),
@@ -210,7 +230,7 @@ def test_decode_validation(lib, kw, status, needle):
     assert st == status, (_lib.status_str(st), _lib.last_error())
     assert needle in _lib.last_error()
     st2, _ = _lib.decode_workspace_size(p)
-    if needle in ("seqlens_k", "aligned"):
+    if needle in ("seqlens_k", "aligned", "4-byte"):
         # sizing the workspace needs shapes only, never the data pointers
         assert st2 == _lib.FA_OK
     else:
@@ -267,3 +287,30 @@ def test_no_unresolved_internal_symbols(lib):
                          check=True).stdout
     undefined = [l.split()[-1] for l in out.splitlines() if l.strip().startswith("U ")]
     assert not [s for s in undefined if s.startswith("_ZN2fa")], undefined
+
+
+def test_decode_paged_limits(lib):
+    # paged: only one page's rows need 32-bit offsets, not the whole capacity
+    pg = dict(block_table=FAKE + 24576, page_size=256, num_pages=1 << 16)
+    p = _decode(batch=1, cache_capacity=1 << 22, pages_per_seq=(1 << 22) // 256,
+                k_stride=[256 * 8 * 128, 8 * 128, 128], v_stride=[256 * 8 * 128, 8 * 128, 128], **pg)
+    st, n = _lib.decode_workspace_size(p)
+    assert st == _lib.FA_OK and n > 0
+    # a page whose rows need more than 32-bit offsets is refused
+    p = _decode(batch=1, cache_capacity=65536, page_size=65536, pages_per_seq=1,
+                block_table=FAKE + 24576, num_pages=2,
+                k_stride=[65536 * 65536, 65536, 128], v_stride=[65536 * 65536, 65536, 128])
+    assert _lib.decode_fwd(p, FAKE, 1 << 40, 0) == _lib.FA_ERR_UNSUPPORTED
+    assert "per page" in _lib.last_error()
+    # the table's entry count must fit int32
+    p = _decode(batch=64, cache_capacity=8192, page_size=16, pages_per_seq=1 << 26,
+                block_table=FAKE + 24576, num_pages=2)
+    assert _lib.decode_workspace_size(p)[0] == _lib.FA_ERR_UNSUPPORTED
+    assert "2^31" in _lib.last_error()
+    # the workspace depends on the logical capacity only, paged or not
+    plain = _lib.decode_workspace_size(_decode())
+    paged = _lib.decode_workspace_size(_decode(block_table=FAKE + 24576, page_size=16,
+                                               pages_per_seq=512, num_pages=40000,
+                                               k_stride=[16 * 8 * 128, 8 * 128, 128],
+                                               v_stride=[16 * 8 * 128, 8 * 128, 128]))
+    assert plain == paged

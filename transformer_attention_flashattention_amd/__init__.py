@@ -135,9 +135,14 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     return out, (lse if return_lse else None)
 
 
-def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys, al=None):
+def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys, al=None,
+                   table=None, capacity=None):
     B, Hq, d = q.shape
     _, cap, Hkv, _ = k_cache.shape
+    if table is not None:
+        # paged: k_cache is the pool [num_pages, page_size, Hkv, d]
+        page_size, pages_per_seq = cap, table.shape[1]
+        cap = pages_per_seq * page_size if capacity is None else int(capacity)
     p = _lib.DecodeParams()
     p.dtype = _dtype_code(q)
     p.batch, p.heads_q, p.heads_kv, p.head_dim = B, Hq, Hkv, d
@@ -157,13 +162,33 @@ def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys,
     if out is not None:
         p.o_stride[:] = [out.stride(0), out.stride(1)]
     p.alibi_slopes = al.data_ptr() if al is not None else None
+    if table is not None:
+        p.block_table = table.data_ptr()
+        p.page_size, p.pages_per_seq, p.num_pages = page_size, pages_per_seq, k_cache.shape[0]
     return p
 
 
+def _block_table(table, B, device):
+    torch = _torch()
+    if table is None:
+        return None
+    if not isinstance(table, torch.Tensor):
+        table = torch.tensor(table, dtype=torch.int32)
+    table = table.to(device=device, dtype=torch.int32).contiguous()
+    if table.dim() != 2 or table.shape[0] != B:
+        raise ValueError(f"block_table must be [{B}, pages_per_seq]")
+    return table
+
+
 def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
-                          chunk_keys: int = 0) -> int:
+                          chunk_keys: int = 0, block_table=None, capacity=None) -> int:
     """Workspace bytes ``decode`` needs for these shapes (host-only)."""
-    p = _decode_params(q, k_cache, v_cache, None, None, None, scale, window, chunk_keys)
+    table = block_table
+    if table is not None and not isinstance(table, _torch().Tensor):
+        table = _torch().tensor(table, dtype=_torch().int32)
+    # sizing reads shapes only; the table's contents stay where they are
+    p = _decode_params(q, k_cache, v_cache, None, None, None, scale, window, chunk_keys,
+                       table=table, capacity=capacity)
     st, n = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     return n
@@ -171,8 +196,8 @@ def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
 
 def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, window: int = -1,
            chunk_keys: int = 0, workspace=None, out=None, lse=None, return_lse: bool = True,
-           alibi_slopes=None):
-    """Single-token decode over a contiguous KV cache.
+           alibi_slopes=None, block_table=None, capacity: Optional[int] = None):
+    """Single-token decode over a KV cache, contiguous or paged.
 
     q: [B, Hq, d]; k_cache, v_cache: [B, capacity, Hkv, d]; seqlens_k: [B]
     valid lengths (the current token already appended).  Returns ``(o, lse)``:
@@ -180,13 +205,20 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     of at least ``decode_workspace_size`` bytes) may be passed to avoid an
     allocation per call.  ``alibi_slopes`` (one value per query head) adds the
     ALiBi bias -slope_h * (L_b - 1 - j).
+
+    Paged cache: with ``block_table`` (int32 [B, pages_per_seq]) the caches are
+    page pools [num_pages, page_size, Hkv, d]; logical row j of sequence b is
+    row j % page_size of page block_table[b, j // page_size].  ``capacity``
+    (default pages_per_seq * page_size) caps the lengths.
     """
     torch = _torch()
     _require_gpu(q, k_cache, v_cache)
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("q must be [B, Hq, d] and caches [B, capacity, Hkv, d]")
+        raise ValueError("q must be [B, Hq, d] and caches [B, capacity, Hkv, d] "
+                         "(or pools [num_pages, page_size, Hkv, d])")
     B, Hq, d = q.shape
-    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+    table = _block_table(block_table, B, q.device)
+    if (table is None and k_cache.shape[0] != B) or k_cache.shape[3] != d:
         raise ValueError("cache shape does not match q")
     if not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("q and the caches must share one dtype")
@@ -201,7 +233,7 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     al = _slopes(alibi_slopes, Hq, dev)
     p = _decode_params(q, k_cache, v_cache, sk, out, lse if return_lse else None, scale, window,
-                       chunk_keys, al)
+                       chunk_keys, al, table, capacity)
     st, need = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     if workspace is None:

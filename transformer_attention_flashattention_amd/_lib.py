@@ -81,6 +81,11 @@ class DecodeParams(ctypes.Structure):
         ("v_stride", _i64x3),
         ("o_stride", _i64x2),
         ("alibi_slopes", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
     ]
 
 

@@ -118,12 +118,19 @@ __device__ __forceinline__ void visible_range(const DecodeArgs &a, int b, int &l
     lo = (a.window_left > 0) ? max(0, L - a.window_left) : 0;
 }
 
-// The visible keys of a sequence are cut into n = ceil((L - lo) / a.chunk)
-// chunks of equal length len (a multiple of 128, at most a.chunk); chunk c
-// covers [lo + c len, min(L, lo + (c + 1) len)) and is never empty.  Equal
-// chunks keep the workgroups of one sequence equally long.
+// First key of the chunk grid: lo itself, or for a paged cache lo rounded
+// down to a whole tile, so that every tile lies inside one page.
+__device__ __forceinline__ int chunk_origin(const DecodeArgs &a, int lo) {
+    return a.block_table ? (lo & ~(KT - 1)) : lo;
+}
+
+// The keys [origin, L) of a sequence are cut into n = ceil((L - origin) /
+// a.chunk) chunks of equal length len (a multiple of 128, at most a.chunk);
+// chunk c covers [origin + c len, min(L, origin + (c + 1) len)) and holds a
+// visible key (origin > lo - 128).  Equal chunks keep the workgroups of one
+// sequence equally long.
 __device__ __forceinline__ void chunking(const DecodeArgs &a, int lo, int L, int &n, int &len) {
-    const int Lv = L - lo;
+    const int Lv = L - chunk_origin(a, lo);
     n = (Lv + a.chunk - 1) / a.chunk;
     len = n > 0 ? (((Lv + n - 1) / n + kDecodeChunkUnit - 1) / kDecodeChunkUnit) * kDecodeChunkUnit : 0;
 }
@@ -133,9 +140,10 @@ __device__ __forceinline__ u32x4 load_nt(const char *base, unsigned off) {
 }
 
 // D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
-// a slice of it); ALIBI: add the per-head linear bias -m (L - 1 - j).  Chunk
-// lengths are multiples of NWAVES * KT.
-template <int D, int GT, bool ALIBI>
+// a slice of it); ALIBI: add the per-head linear bias -m (L - 1 - j); PAGED:
+// the cache is a pool of pages named by a block table.  Chunk lengths are
+// multiples of NWAVES * KT.
+template <int D, int GT, bool ALIBI, bool PAGED>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
     constexpr int SKP = 64 / SL;             // keys per score pass
@@ -196,16 +204,18 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     int lo, L, nchunks, C;
     visible_range(a, b, lo, L);
     chunking(a, lo, L, nchunks, C);
-    const int k0 = lo + chunk * C;
+    const int k0 = chunk_origin(a, lo) + chunk * C;
     const int h0 = kvh * a.group + hg * GT;        // first query head of this workgroup
-    // keys this workgroup owns (never empty)
-    const int jlo = k0, jhi = min(L, k0 + C);
+    // visible keys this workgroup owns (never empty)
+    const int jlo = max(k0, lo), jhi = min(L, k0 + C);
 
     // wavefront index, made provably uniform so that branches on it are scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const char *Kp = (const char *)((const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh);
-    const char *Vp = (const char *)((const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh);
-    // row offsets within one sequence fit 32 bits (checked on the host)
+    // contiguous cache: the sequence's rows of this KV head (paged: the
+    // pool's page 0, replaced per tile)
+    const char *Kp = (const char *)((const unsigned short *)a.k + (PAGED ? 0 : b * a.k_sb) + kvh * a.k_sh);
+    const char *Vp = (const char *)((const unsigned short *)a.v + (PAGED ? 0 : b * a.v_sb) + kvh * a.v_sh);
+    // row offsets within one sequence (one page) fit 32 bits (checked on the host)
     const unsigned k_row = (unsigned)a.k_ss * 2u, v_row = (unsigned)a.v_ss * 2u;
     const int s_key = lane / SL, s_sub = lane % SL;    // score layout
     const int v_key = lane / VL, v_sub = lane % VL;    // value layout
@@ -252,21 +262,46 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     // Keys outside [jlo, jhi) load a clamped, valid row instead (finite data;
     // the score mask then gives them p = 0), so every load is unconditional and
     // the compiler can wait for exactly the current tile's loads.
+    //
+    // Paged cache: a tile starts at a multiple of KT keys (chunk_origin) and a
+    // page holds a multiple of KT rows, so the keys of a tile share one page,
+    // and so do their clamped stand-ins: they are jlo or jhi - 1, which lie in
+    // the tile whenever any of its keys is visible, and otherwise every key of
+    // the tile clamps to the same one.  That page is the page of the tile's
+    // first key clamped to [jlo, jhi); the wavefront reads its table entry
+    // (one uniform load) and addresses the rows inside it.
     u32x4 kb[NBUF][SP][2], vb[NBUF][VP];
     auto load = [&](int t, u32x4 (&kt)[SP][2], u32x4 (&vt)[VP]) __attribute__((always_inline)) {
         const int t0 = tile_key0(t);
+        const char *kbase = Kp, *vbase = Vp;
+        int row0 = 0;                                  // logical key of row 0 at kbase
+        if constexpr (PAGED) {
+            const int anchor = min(max(t0, jlo), jhi - 1);
+            const int pg = anchor / a.page_size;
+            // the table is read-only for the whole launch: reading it through
+            // the constant address space gives a scalar load whose wait the
+            // compiler tracks itself (a generic pointer gives a flat load,
+            // which would also wait for every K/V load in flight)
+            const __attribute__((address_space(4))) int32_t *table =
+                (const __attribute__((address_space(4))) int32_t *)a.block_table;
+            int phys = table[(int64_t)b * a.pages_per_seq + pg];
+            phys = min(max(phys, 0), a.num_pages - 1);
+            kbase = Kp + (int64_t)phys * a.k_sb * 2;
+            vbase = Vp + (int64_t)phys * a.v_sb * 2;
+            row0 = pg * a.page_size;
+        }
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
             const int j = min(max(t0 + p * SKP + s_key, jlo), jhi - 1);
             // each load instruction covers one contiguous half of every row it touches
-            const unsigned off = (unsigned)j * k_row + s_sub * 16;
-            kt[p][0] = load_nt(Kp, off);
-            kt[p][1] = load_nt(Kp, off + D);
+            const unsigned off = (unsigned)(j - row0) * k_row + s_sub * 16;
+            kt[p][0] = load_nt(kbase, off);
+            kt[p][1] = load_nt(kbase, off + D);
         }
 #pragma unroll
         for (int p = 0; p < VP; ++p) {
             const int j = min(max(t0 + p * VKP + v_key, jlo), jhi - 1);
-            vt[p] = load_nt(Vp, (unsigned)j * v_row + v_sub * 16);
+            vt[p] = load_nt(vbase, (unsigned)(j - row0) * v_row + v_sub * 16);
         }
     };
     auto compute = [&](int t, const u32x4 (&kt)[SP][2], const u32x4 (&vt)[VP]) __attribute__((always_inline)) {
@@ -505,11 +540,17 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
         a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Lsum)) * LN2 : -INFINITY;
 }
 
+template <int D, int GT, bool ALIBI>
+void launch_split_paged(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+    if (a.block_table) hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, true>), grid, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, false>), grid, dim3(NTHREADS), 0, s, a);
+}
+
 template <int D, int GT>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)(a.heads_kv * a.head_groups) * a.batch * a.max_chunks);
-    if (a.alibi) hipLaunchKernelGGL((decode_split_kernel<D, GT, true>), grid, dim3(NTHREADS), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<D, GT, false>), grid, dim3(NTHREADS), 0, s, a);
+    if (a.alibi) launch_split_paged<D, GT, true>(a, grid, s);
+    else launch_split_paged<D, GT, false>(a, grid, s);
     return hipGetLastError();
 }
 

@@ -97,7 +97,23 @@ fa_status validate_decode(const fa_decode_params *p) {
         (p->chunk_keys < 0 || p->chunk_keys % fa::kDecodeChunkUnit != 0 || p->chunk_keys > 65536))
         return fail(FA_ERR_UNSUPPORTED, "chunk_keys must be 0 or a multiple of %d up to 65536 (got %d)",
                     fa::kDecodeChunkUnit, p->chunk_keys);
-    if (p->reserved0 != 0) return fail(FA_ERR_INVALID_ARG, "reserved0 must be 0");
+    if (p->reserved0 != 0 || p->reserved1 != 0)
+        return fail(FA_ERR_INVALID_ARG, "reserved0 and reserved1 must be 0");
+    if (p->block_table) {
+        if (p->page_size < fa::kDecodePageUnit || p->page_size > 65536 ||
+            p->page_size % fa::kDecodePageUnit != 0)
+            return fail(FA_ERR_UNSUPPORTED, "page_size must be a multiple of %d in [%d, 65536] (got %d)",
+                        fa::kDecodePageUnit, fa::kDecodePageUnit, p->page_size);
+        if (p->pages_per_seq < 1 || p->num_pages < 1)
+            return fail(FA_ERR_INVALID_ARG, "pages_per_seq and num_pages must be >= 1 with a block_table");
+        if (p->cache_capacity > (int64_t)p->pages_per_seq * p->page_size)
+            return fail(FA_ERR_INVALID_ARG, "cache_capacity (%d) exceeds pages_per_seq x page_size (%lld)",
+                        p->cache_capacity, (long long)p->pages_per_seq * p->page_size);
+        if ((int64_t)p->batch * p->pages_per_seq > 0x7fffffffLL)
+            return fail(FA_ERR_UNSUPPORTED, "block_table has more than 2^31 - 1 entries");
+    } else if (p->page_size != 0 || p->pages_per_seq != 0 || p->num_pages != 0) {
+        return fail(FA_ERR_INVALID_ARG, "page_size, pages_per_seq and num_pages must be 0 without a block_table");
+    }
     FA_TRY(check_scale(p->softmax_scale));
     FA_TRY(check_strides("q", p->q_stride, 2, 8));
     FA_TRY(check_strides("k", p->k_stride, 3, 8));
@@ -115,6 +131,8 @@ fa_status validate_decode_pointers(const fa_decode_params *p) {
         return fail(FA_ERR_UNSUPPORTED, "q, k_cache and v_cache must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(p->o) & 1u) != 0)
         return fail(FA_ERR_INVALID_ARG, "o must be 2-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(p->block_table) & 3u) != 0)
+        return fail(FA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
     return FA_OK;
 }
 
@@ -224,9 +242,12 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     if (workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     const int max_chunks = (p->cache_capacity + chunk - 1) / chunk;
-    // the split kernel addresses the rows of one sequence with 32-bit byte offsets
-    if ((int64_t)p->cache_capacity * std::max(p->k_stride[1], p->v_stride[1]) * 2 > 0xffffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "cache_capacity x seq stride exceeds 4 GiB per sequence");
+    // the split kernel addresses the rows of one sequence (one page when
+    // paged) with 32-bit byte offsets
+    const int64_t rows_addressed = p->block_table ? p->page_size : p->cache_capacity;
+    if (rows_addressed * std::max(p->k_stride[1], p->v_stride[1]) * 2 > 0xffffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, p->block_table ? "page_size x seq stride exceeds 4 GiB per page"
+                                                       : "cache_capacity x seq stride exceeds 4 GiB per sequence");
     if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL ||
         (int64_t)p->heads_kv * (group / gt) * p->batch * max_chunks > 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
@@ -244,6 +265,8 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     a.scale_log2 = p->softmax_scale * kLog2e;
     a.scale = p->softmax_scale;
     a.alibi = p->alibi_slopes;
+    a.block_table = p->block_table;
+    a.page_size = p->page_size; a.pages_per_seq = p->pages_per_seq; a.num_pages = p->num_pages;
     const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
     const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = static_cast<float *>(workspace);

@@ -45,6 +45,8 @@ struct DecodeArgs {
     float *ws_ml;                  // [batch, heads_q, max_chunks, 2] fp32 (m, l)
     const float *alibi;            // ALiBi slopes [heads_q] or null
     float scale;                   // softmax_scale
+    const int32_t *block_table;    // paged cache: [batch, pages_per_seq], or null (contiguous)
+    int32_t page_size, pages_per_seq, num_pages;
 };
 
 // Each launcher enqueues its kernel(s) and returns the launch status.
@@ -56,6 +58,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_w
 // Tile sizes the launchers use (also needed by the host for grid sizing).
 constexpr int kPrefillBM = 256;    // query rows per workgroup (bf16 path)
 constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
-constexpr int kDecodeChunkUnit = 128;  // decode chunks: 4 wavefronts x 32-key tiles
+constexpr int kDecodeChunkUnit = 128;  // decode chunks: whole rounds of 4 wavefronts x 16-key tiles
+constexpr int kDecodePageUnit = 16;   // paged cache: page sizes are multiples of one tile
 
 }  // namespace fa

@@ -295,3 +295,14 @@ def make_workload(idx: int):
                             w.pop("Hkv"), w.pop("d"), w.pop("dtype"), **w)
     return make_decode(seed, w.pop("B"), w.pop("Hq"), w.pop("Hkv"), w.pop("d"),
                        w.pop("capacity"), w.pop("len_range"), w.pop("dtype"), **w)
+
+
+def make_workload_paged(idx: int, page_size: int) -> PagedDecodeProblem:
+    """A named decode workload with its cache in a paged pool (same logical
+    rows as :func:`make_workload` for that index)."""
+    w = dict(WORKLOADS[idx])
+    if w.pop("kind") != "decode":
+        raise ValueError("only decode workloads have a paged form")
+    w.pop("name")
+    return make_decode_paged(w.pop("seed"), w.pop("B"), w.pop("Hq"), w.pop("Hkv"), w.pop("d"),
+                             w.pop("capacity"), w.pop("len_range"), page_size, w.pop("dtype"), **w)
