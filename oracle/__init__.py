@@ -5,5 +5,5 @@ leg may import anything under ``oracle/``.  The library's product path
 (the C ABI in ``include/fa.h`` and its Python binding) never calls it, and
 the two share no code.
 """
-from .attention import (alibi_bias, attention, decode, decode_paged, gather_paged,  # noqa: F401
-                        visible, visible_matrix)
+from .attention import (alibi_bias, attention, decode, decode_paged, dequantize_kv,  # noqa: F401
+                        fp8_e4m3_value, gather_paged, visible, visible_matrix)

@@ -57,7 +57,16 @@ notes):
   ``p * page_size .. (p + 1) * page_size - 1``.  The attention computed over
   the gathered rows is the decode above, unchanged.  The page's other
   strategies (keeping only "important" rows) change the result and have no
-  stated criterion; they are not part of this oracle.
+  stated criterion; they are not part of this oracle;
+* quantized KV cache (INT8 input with calibration, the jsqmd.com page,
+  section 五 on mixed precision; kv_quant_sparse_flash_attention, named in
+  the BERT page's preface).  Neither page gives a format or a scale
+  convention.  The reading here: each cached K and V element is an 8-bit
+  float code in the OCP FP8 E4M3 encoding (E4M3FN: 1 sign bit, 4 exponent
+  bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN,
+  largest finite value 448), with one fp32 scale per KV head for K and one
+  for V; the element's value is ``scale * E4M3(code)``.  Attention over the
+  dequantized cache is the decode above, unchanged.
 
 Every function here is pinned in ``tests/test_oracle.py`` against closed
 forms, brute force on tiny integer inputs, library routines and invariants.
@@ -250,3 +259,25 @@ def decode_paged(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         o[bi] = ob[0, 0]
         lse[bi] = lb[0, :, 0]
     return o, lse
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Exact float64 values of OCP FP8 E4M3 (E4M3FN) codes (uint8).
+
+    Exponent field e (4 bits, bias 7) and mantissa m (3 bits): e = 0 is
+    subnormal, m / 8 * 2^-6; otherwise (1 + m / 8) * 2^(e - 7); e = 15 with
+    m = 7 is NaN (the format has no infinities).  The sign bit negates.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((c & 0x80) != 0, -mag, mag)
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, val)
+
+
+def dequantize_kv(codes, scales) -> np.ndarray:
+    """Values of a quantized K or V cache: codes [..., Hkv, d] (uint8 E4M3),
+    scales [Hkv] (float32, one per KV head); value = scale[h] * E4M3(code)."""
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return fp8_e4m3_value(codes) * sc[:, None]

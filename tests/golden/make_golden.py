@@ -22,6 +22,8 @@ def main():
         "decode_small": workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16").sha256(),
         "decode_paged_small": workloads.make_decode_paged(6, 3, 4, 2, 64, 300, (1, 300), 16,
                                                           "bf16").sha256(),
+        "decode_fp8_small": workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16",
+                                                  kv_dtype="fp8_e4m3").sha256(),
     }
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "input_hashes.json")
     with open(path, "w") as f:

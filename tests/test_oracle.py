@@ -423,6 +423,8 @@ def test_generator_hashes_are_stable():
     assert dec.sha256() == stored["decode_small"]
     pdec = workloads.make_decode_paged(6, 3, 4, 2, 64, 300, (1, 300), 16, "bf16")
     assert pdec.sha256() == stored["decode_paged_small"]
+    fdec = workloads.make_decode(6, 3, 4, 2, 64, 300, (1, 300), "bf16", kv_dtype="fp8_e4m3")
+    assert fdec.sha256() == stored["decode_fp8_small"]
 
 
 def test_nan_on_visible_key_propagates():
@@ -621,3 +623,77 @@ def test_paged_generator_holds_the_contiguous_rows():
         used = -(-int(p.seqlens_k[b]) // 16)
         for e in p.block_table[b, used:]:
             assert (p.k_pool[e] == workloads.BF16_QNAN).all()
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 KV cache: code values and dequantized decode
+# ---------------------------------------------------------------------------
+# code -> value, read off the E4M3FN bit layout by hand
+E4M3_LITERALS = {
+    0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+    0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x40: 2.0, 0x47: 3.75, 0x77: 240.0, 0x78: 256.0,
+    0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0,
+}
+
+
+def test_fp8_e4m3_literal_codes():
+    for code, val in E4M3_LITERALS.items():
+        got = oracle.fp8_e4m3_value(np.array([code], dtype=np.uint8))[0]
+        assert got == val and np.signbit(got) == np.signbit(val), hex(code)
+    nan = oracle.fp8_e4m3_value(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.isnan(nan).all()
+
+
+def test_fp8_e4m3_all_codes_match_torch_and_order():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_e4m3_value(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ours)
+    assert np.array_equal(ours[fin], ref[fin])
+    pos = ours[:0x7F]
+    assert np.all(np.diff(pos) > 0)                    # 0x00 .. 0x7E strictly increasing
+    assert np.array_equal(ours[0x80:0xFF], -pos)       # the sign bit only negates
+
+
+def test_dequantized_decode_scaling_laws():
+    """A K scale multiplies every score (the same as scaling softmax_scale);
+    a V scale multiplies O and leaves LSE alone; constant K codes give the
+    mean of the dequantized V rows."""
+    prob = workloads.make_decode(45, 3, 8, 2, 16, 80, (1, 80), "bf16", kv_dtype="fp8_e4m3")
+    q = workloads.to_f64(prob.q, "bf16")
+    ks, vs = prob.k_scale, prob.v_scale
+    k = oracle.dequantize_kv(prob.k_cache, ks)
+    v = oracle.dequantize_kv(prob.v_cache, vs)
+    o1, l1 = oracle.decode(q, k, v, prob.seqlens_k, scale=0.25)
+    o2, l2 = oracle.decode(q, oracle.dequantize_kv(prob.k_cache, 2 * ks), v, prob.seqlens_k,
+                           scale=0.125)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
+    o3, l3 = oracle.decode(q, k, oracle.dequantize_kv(prob.v_cache, 2 * vs), prob.seqlens_k,
+                           scale=0.25)
+    np.testing.assert_allclose(o3, 2 * o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l3, l1, rtol=0, atol=0)
+    const = np.where(prob.k_cache == workloads.FP8_E4M3_QNAN, prob.k_cache, np.uint8(0x38))
+    o4, l4 = oracle.decode(q, oracle.dequantize_kv(const, ks), v, prob.seqlens_k, scale=0.25)
+    for b in range(3):
+        L = int(prob.seqlens_k[b])
+        for h in range(8):
+            np.testing.assert_allclose(o4[b, h], v[b, :L, h // 4].mean(axis=0), atol=1e-12)
+            assert abs(l4[b, h] - (0.25 * float(ks[h // 4]) * q[b, h].sum() + math.log(L))) < 1e-12
+
+
+def test_fp8_generator_codes_round_to_nearest():
+    """The generator's codes hold the drawn values to E4M3's half-step, and
+    each head's largest magnitude lands on +-448."""
+    prob = workloads.make_decode(46, 2, 4, 2, 16, 64, (64, 64), "bf16", kv_dtype="fp8_e4m3")
+    raw = workloads.make_decode(46, 2, 4, 2, 16, 64, (64, 64), "f32")
+    for codes, sc, x in ((prob.k_cache, prob.k_scale, raw.k_cache),
+                         (prob.v_cache, prob.v_scale, raw.v_cache)):
+        vals = oracle.fp8_e4m3_value(codes)
+        y = x.astype(np.float64) / sc.astype(np.float64)[:, None]
+        # E4M3 step at |y|: 2^(floor(log2 |y|) - 3), at least the subnormal step 2^-9
+        step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))), -6) - 3)
+        assert np.all(np.abs(vals - y) <= 0.5 * step * (1 + 1e-6))
+        for h in range(2):
+            assert np.abs(vals[:, :, h]).max() == 448.0

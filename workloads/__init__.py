@@ -109,11 +109,15 @@ class DecodeProblem:
     seqlens_k: np.ndarray            # int32 [B]
     scale: float
     window_left: int = -1
+    kv_dtype: Optional[str] = None   # None: caches in dtype; "fp8_e4m3": uint8 codes
+    k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (fp8 caches)
+    v_scale: Optional[np.ndarray] = None
 
     def sha256(self) -> str:
         h = hashlib.sha256()
-        for a in (self.q, self.k_cache, self.v_cache, self.seqlens_k):
-            h.update(np.ascontiguousarray(a).tobytes())
+        for a in (self.q, self.k_cache, self.v_cache, self.seqlens_k, self.k_scale, self.v_scale):
+            if a is not None:
+                h.update(np.ascontiguousarray(a).tobytes())
         return h.hexdigest()
 
 
@@ -154,35 +158,79 @@ def make_prefill(seed: int, B: int, Nq: int, Nk: int, Hq: int, Hkv: int,
                           scale, causal, window_left, seqlens_q, seqlens_k)
 
 
-def make_decode(seed: int, B: int, Hq: int, Hkv: int, d: int, capacity: int,
-                len_range: tuple, dtype: str = "bf16", *,
-                scale: Optional[float] = None, window_left: int = -1,
-                lengths: Optional[np.ndarray] = None) -> DecodeProblem:
-    """Draw a single-token decode problem over a contiguous BSHD KV cache.
+FP8_E4M3_QNAN = np.uint8(0x7F)
+FP8_E4M3_MAX = 448.0
 
-    Lengths are drawn first (uniform in ``len_range``, inclusive) unless given,
-    then Q ``[B, Hq, d]``, then per sequence its valid K rows and V rows.
-    Cache rows at or beyond the length hold NaN.
-    """
-    rng = np.random.default_rng(seed)
+
+def f32_to_fp8_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to OCP FP8 E4M3 codes (nearest, ties to even), by
+    torch's float8_e4m3fn cast.  Inputs must lie within +-448."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _draw_decode(rng, B, Hq, Hkv, d, capacity, len_range, lengths):
+    """Lengths (unless given), then Q, then per sequence its K rows and V rows."""
     if lengths is None:
         lo, hi = len_range
         lengths = rng.integers(lo, hi + 1, size=B).astype(np.int32)
     lengths = np.asarray(lengths, dtype=np.int32)
     q = rng.standard_normal((B, Hq, d), dtype=np.float32)
-    if dtype == "bf16":
-        kc = np.full((B, capacity, Hkv, d), BF16_QNAN, dtype=np.uint16)
-        vc = np.full((B, capacity, Hkv, d), BF16_QNAN, dtype=np.uint16)
-    else:
-        kc = np.full((B, capacity, Hkv, d), np.nan, dtype=np.float32)
-        vc = np.full((B, capacity, Hkv, d), np.nan, dtype=np.float32)
+    rows_k, rows_v = [], []
     for b in range(B):
         L = int(min(max(lengths[b], 0), capacity))
-        kc[b, :L] = _store(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype)
-        vc[b, :L] = _store(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype)
+        rows_k.append(rng.standard_normal((L, Hkv, d), dtype=np.float32))
+        rows_v.append(rng.standard_normal((L, Hkv, d), dtype=np.float32))
+    return lengths, q, rows_k, rows_v
+
+
+def _store_rows(rows, dtype, kv_dtype, Hkv):
+    """Stored form of every sequence's rows, the NaN fill value and the
+    per-KV-head scales (fp8: scale = max |x| over the head's rows / 448, in
+    fp32, and codes = E4M3(x / scale))."""
+    if kv_dtype is None:
+        fill = BF16_QNAN if dtype == "bf16" else np.float32(np.nan)
+        return [_store(r, dtype) for r in rows], fill, None
+    if kv_dtype != "fp8_e4m3":
+        raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
+    amax = np.zeros(Hkv, dtype=np.float32)
+    for r in rows:
+        if r.shape[0]:
+            amax = np.maximum(amax, np.abs(r).max(axis=(0, 2)))
+    scales = np.where(amax > 0, amax / np.float32(FP8_E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    codes = [f32_to_fp8_e4m3_codes(np.clip(r / scales[None, :, None], -FP8_E4M3_MAX, FP8_E4M3_MAX))
+             for r in rows]
+    return codes, FP8_E4M3_QNAN, scales
+
+
+def make_decode(seed: int, B: int, Hq: int, Hkv: int, d: int, capacity: int,
+                len_range: tuple, dtype: str = "bf16", *,
+                scale: Optional[float] = None, window_left: int = -1,
+                lengths: Optional[np.ndarray] = None,
+                kv_dtype: Optional[str] = None) -> DecodeProblem:
+    """Draw a single-token decode problem over a contiguous BSHD KV cache.
+
+    Lengths are drawn first (uniform in ``len_range``, inclusive) unless given,
+    then Q ``[B, Hq, d]``, then per sequence its valid K rows and V rows.
+    Cache rows at or beyond the length hold NaN.  ``kv_dtype="fp8_e4m3"``
+    stores K and V as E4M3 codes with one fp32 scale per KV head each (the
+    same draws, so the same logical cache up to quantization); Q stays in
+    ``dtype``.
+    """
+    rng = np.random.default_rng(seed)
+    lengths, q, rows_k, rows_v = _draw_decode(rng, B, Hq, Hkv, d, capacity, len_range, lengths)
+    sk, fill, k_scale = _store_rows(rows_k, dtype, kv_dtype, Hkv)
+    sv, _, v_scale = _store_rows(rows_v, dtype, kv_dtype, Hkv)
+    kc = np.full((B, capacity, Hkv, d), fill, dtype=np.asarray(fill).dtype)
+    vc = np.full((B, capacity, Hkv, d), fill, dtype=np.asarray(fill).dtype)
+    for b in range(B):
+        kc[b, :sk[b].shape[0]] = sk[b]
+        vc[b, :sv[b].shape[0]] = sv[b]
     if scale is None:
         scale = float(np.float32(1.0 / np.sqrt(d)))
-    return DecodeProblem(dtype, _store(q, dtype), kc, vc, lengths, scale, window_left)
+    return DecodeProblem(dtype, _store(q, dtype), kc, vc, lengths, scale, window_left,
+                         kv_dtype, k_scale, v_scale)
 
 
 @dataclasses.dataclass
@@ -195,6 +243,9 @@ class PagedDecodeProblem:
     seqlens_k: np.ndarray            # int32 [B]
     scale: float
     window_left: int = -1
+    kv_dtype: Optional[str] = None
+    k_scale: Optional[np.ndarray] = None
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def page_size(self) -> int:
@@ -202,8 +253,10 @@ class PagedDecodeProblem:
 
     def sha256(self) -> str:
         h = hashlib.sha256()
-        for a in (self.q, self.k_pool, self.v_pool, self.block_table, self.seqlens_k):
-            h.update(np.ascontiguousarray(a).tobytes())
+        for a in (self.q, self.k_pool, self.v_pool, self.block_table, self.seqlens_k,
+                  self.k_scale, self.v_scale):
+            if a is not None:
+                h.update(np.ascontiguousarray(a).tobytes())
         return h.hexdigest()
 
     @property
@@ -215,7 +268,7 @@ def make_decode_paged(seed: int, B: int, Hq: int, Hkv: int, d: int, capacity: in
                       len_range: tuple, page_size: int, dtype: str = "bf16", *,
                       scale: Optional[float] = None, window_left: int = -1,
                       lengths: Optional[np.ndarray] = None,
-                      spare_pages: int = 1) -> PagedDecodeProblem:
+                      spare_pages: int = 1, kv_dtype: Optional[str] = None) -> PagedDecodeProblem:
     """Draw a single-token decode problem over a paged KV cache.
 
     The draws are those of :func:`make_decode` with the same arguments
@@ -231,40 +284,32 @@ def make_decode_paged(seed: int, B: int, Hq: int, Hkv: int, d: int, capacity: in
     if spare_pages < 1:
         raise ValueError("spare_pages must be >= 1")
     rng = np.random.default_rng(seed)
-    if lengths is None:
-        lo, hi = len_range
-        lengths = rng.integers(lo, hi + 1, size=B).astype(np.int32)
-    lengths = np.asarray(lengths, dtype=np.int32)
-    q = rng.standard_normal((B, Hq, d), dtype=np.float32)
+    lengths, q, rows_k, rows_v = _draw_decode(rng, B, Hq, Hkv, d, capacity, len_range, lengths)
+    sk, fill, k_scale = _store_rows(rows_k, dtype, kv_dtype, Hkv)
+    sv, _, v_scale = _store_rows(rows_v, dtype, kv_dtype, Hkv)
     P = int(page_size)
     per_seq = -(-capacity // P)
-    used = [-(-int(min(max(L, 0), capacity)) // P) for L in lengths]
+    used = [-(-r.shape[0] // P) for r in sk]
     n_pages = sum(used) + spare_pages
-    fill = BF16_QNAN if dtype == "bf16" else np.float32(np.nan)
-    sdt = np.uint16 if dtype == "bf16" else np.float32
-    kp = np.full((n_pages, P, Hkv, d), fill, dtype=sdt)
-    vp = np.full((n_pages, P, Hkv, d), fill, dtype=sdt)
-    rows_k, rows_v = [], []
-    for b in range(B):
-        L = int(min(max(lengths[b], 0), capacity))
-        rows_k.append(_store(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype))
-        rows_v.append(_store(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype))
+    kp = np.full((n_pages, P, Hkv, d), fill, dtype=np.asarray(fill).dtype)
+    vp = np.full((n_pages, P, Hkv, d), fill, dtype=np.asarray(fill).dtype)
     order = rng.permutation(n_pages).astype(np.int32)
     spare = order[sum(used)]
     table = np.full((B, per_seq), spare, dtype=np.int32)
     nxt = 0
     for b in range(B):
-        L = rows_k[b].shape[0]
+        L = sk[b].shape[0]
         for pg in range(used[b]):
             phys = order[nxt]
             nxt += 1
             table[b, pg] = phys
             n = min(P, L - pg * P)
-            kp[phys, :n] = rows_k[b][pg * P:pg * P + n]
-            vp[phys, :n] = rows_v[b][pg * P:pg * P + n]
+            kp[phys, :n] = sk[b][pg * P:pg * P + n]
+            vp[phys, :n] = sv[b][pg * P:pg * P + n]
     if scale is None:
         scale = float(np.float32(1.0 / np.sqrt(d)))
-    return PagedDecodeProblem(dtype, _store(q, dtype), kp, vp, table, lengths, scale, window_left)
+    return PagedDecodeProblem(dtype, _store(q, dtype), kp, vp, table, lengths, scale, window_left,
+                              kv_dtype, k_scale, v_scale)
 
 
 # --------------------------------------------------------------------------
