@@ -58,6 +58,13 @@ typedef enum {
     FA_DTYPE_BF16 = 1         /* bf16 in, bf16 MFMA with fp32 accumulation, bf16 out */
 } fa_dtype;
 
+/* Storage of a decode KV cache (fa_decode_params.kv_format). */
+typedef enum {
+    FA_KV_PLAIN = 0,          /* K and V in the call's dtype                        */
+    FA_KV_FP8_E4M3 = 1        /* K and V as OCP FP8 E4M3 codes, one fp32 scale per
+                                 KV head for each (see fa_decode_params)            */
+} fa_kv_format;
+
 /*
  * Prefill / encoder attention: fa_prefill_fwd
  * -------------------------------------------
@@ -177,6 +184,17 @@ typedef struct {
  * times the row stride of k and v below 2^31 elements.  With block_table
  * NULL, page_size, pages_per_seq and num_pages must be 0.
  *
+ * FP8 KV cache (kv_format = FA_KV_FP8_E4M3): the quantized KV cache named on
+ * the pages (INT8 input with calibration, jsqmd.com page, section 五;
+ * kv_quant_sparse_flash_attention, BERT page preface), which fix no format.
+ * Each cached element is one byte, an OCP FP8 E4M3 code (E4M3FN: bias 7, no
+ * infinities, S.1111.111 is NaN, largest finite value 448), and its value is
+ * k_scale[kvh] * E4M3(code) for K and v_scale[kvh] * E4M3(code) for V, with
+ * k_scale and v_scale device fp32 arrays [heads_kv] (read on the device, not
+ * validated).  q and o stay bf16.  k/v strides count elements (= bytes) and
+ * must be multiples of 16.  Works with the contiguous and the paged layout.
+ * With FA_KV_PLAIN, k_scale and v_scale must be NULL.
+ *
  * Requirements: dtype FA_DTYPE_BF16; head_dim in {64, 128};
  * heads_q % heads_kv == 0; cache_capacity >= 1; softmax_scale finite and > 0.
  */
@@ -207,6 +225,10 @@ typedef struct {
     int32_t pages_per_seq;               /* block_table row length, else 0       */
     int32_t num_pages;                   /* pages in each pool, else 0           */
     int32_t reserved1;                   /* must be 0                            */
+    int32_t kv_format;                   /* fa_kv_format                          */
+    int32_t reserved2;                   /* must be 0                            */
+    const float *k_scale;                /* device fp32 [heads_kv] (FP8) or NULL */
+    const float *v_scale;                /* device fp32 [heads_kv] (FP8) or NULL */
 } fa_decode_params;
 
 /* Enqueue the prefill forward pass.  Returns FA_OK, FA_ERR_INVALID_ARG,
@@ -234,7 +256,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10200
+#define FA_ABI_VERSION 10300
 
 #ifdef __cplusplus
 }

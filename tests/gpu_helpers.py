@@ -132,3 +132,47 @@ def oracle_decode_paged(pp, batches=None, alibi_slopes=None, capacity=None):
                                _exact_f32(pp.v_pool, pp.dtype), pp.block_table, seqlens,
                                scale=pp.scale, window_left=pp.window_left, batches=batches,
                                alibi_slopes=alibi_slopes)
+
+
+def fp8_tensor(codes):
+    """uint8 E4M3 codes as a torch.float8_e4m3fn device tensor (same bytes)."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(DEV).view(
+        torch.float8_e4m3fn)
+
+
+def run_decode_fp8(dp, **kw):
+    q = dev_tensor(dp.q, dp.dtype)
+    kc, vc = fp8_tensor(dp.k_cache), fp8_tensor(dp.v_cache)
+    sk = torch.from_numpy(dp.seqlens_k).to(DEV)
+    o, lse = fa.decode(q, kc, vc, sk, scale=dp.scale, window=dp.window_left,
+                       k_scale=torch.from_numpy(dp.k_scale).to(DEV),
+                       v_scale=torch.from_numpy(dp.v_scale).to(DEV), **kw)
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_decode_fp8(dp, alibi_slopes=None):
+    return oracle.decode(workloads.to_f64(dp.q, dp.dtype),
+                         oracle.dequantize_kv(dp.k_cache, dp.k_scale),
+                         oracle.dequantize_kv(dp.v_cache, dp.v_scale), dp.seqlens_k,
+                         scale=dp.scale, window_left=dp.window_left, alibi_slopes=alibi_slopes)
+
+
+def run_decode_paged_fp8(pp, **kw):
+    q = dev_tensor(pp.q, pp.dtype)
+    kp, vp = fp8_tensor(pp.k_pool), fp8_tensor(pp.v_pool)
+    sk = torch.from_numpy(pp.seqlens_k).to(DEV)
+    table = torch.from_numpy(pp.block_table).to(DEV)
+    o, lse = fa.decode(q, kp, vp, sk, scale=pp.scale, window=pp.window_left, block_table=table,
+                       k_scale=torch.from_numpy(pp.k_scale).to(DEV),
+                       v_scale=torch.from_numpy(pp.v_scale).to(DEV), **kw)
+    torch.cuda.synchronize()
+    return to_np(o), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_decode_paged_fp8(pp, alibi_slopes=None):
+    return oracle.decode_paged(workloads.to_f64(pp.q, pp.dtype),
+                               oracle.dequantize_kv(pp.k_pool, pp.k_scale),
+                               oracle.dequantize_kv(pp.v_pool, pp.v_scale), pp.block_table,
+                               pp.seqlens_k, scale=pp.scale, window_left=pp.window_left,
+                               alibi_slopes=alibi_slopes)

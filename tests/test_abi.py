@@ -70,7 +70,8 @@ int main(void) {
   F(fa_decode_params, seqlens_k) F(fa_decode_params, q_stride) F(fa_decode_params, k_stride)
   F(fa_decode_params, o_stride) F(fa_prefill_params, alibi_slopes) F(fa_decode_params, alibi_slopes)
   F(fa_decode_params, block_table) F(fa_decode_params, page_size) F(fa_decode_params, pages_per_seq)
-  F(fa_decode_params, num_pages) F(fa_decode_params, reserved1)
+  F(fa_decode_params, num_pages) F(fa_decode_params, reserved1) F(fa_decode_params, kv_format)
+  F(fa_decode_params, reserved2) F(fa_decode_params, k_scale) F(fa_decode_params, v_scale)
   return 0;
 }
 """
@@ -202,6 +203,15 @@ def _decode(**kw):
     (dict(chunk_keys=65536 + 128), _lib.FA_ERR_UNSUPPORTED, "chunk_keys"),
     (dict(reserved0=1), _lib.FA_ERR_INVALID_ARG, "reserved0"),
     (dict(reserved1=1), _lib.FA_ERR_INVALID_ARG, "reserved1"),
+    (dict(reserved2=1), _lib.FA_ERR_INVALID_ARG, "reserved2"),
+    # FP8 cache format
+    (dict(kv_format=2), _lib.FA_ERR_INVALID_ARG, "kv_format"),
+    (dict(k_scale=FAKE + 28672), _lib.FA_ERR_INVALID_ARG, "FA_KV_PLAIN"),
+    (dict(kv_format=1, k_scale=FAKE + 28672, v_scale=FAKE + 28800,
+          k_stride=[8192 * 8 * 128, 8 * 128 + 8, 128]), _lib.FA_ERR_UNSUPPORTED, "k_stride"),
+    (dict(kv_format=1, k_scale=None, v_scale=FAKE + 28800), _lib.FA_ERR_INVALID_ARG, "non-NULL"),
+    (dict(kv_format=1, k_scale=FAKE + 28674, v_scale=FAKE + 28800), _lib.FA_ERR_INVALID_ARG,
+     "4-byte aligned"),
     # paged-cache fields without a table, and bad paged parameters
     (dict(page_size=16), _lib.FA_ERR_INVALID_ARG, "without a block_table"),
     (dict(num_pages=4), _lib.FA_ERR_INVALID_ARG, "without a block_table"),
@@ -230,7 +240,7 @@ def test_decode_validation(lib, kw, status, needle):
     assert st == status, (_lib.status_str(st), _lib.last_error())
     assert needle in _lib.last_error()
     st2, _ = _lib.decode_workspace_size(p)
-    if needle in ("seqlens_k", "aligned", "4-byte"):
+    if needle in ("seqlens_k", "aligned", "4-byte", "non-NULL", "4-byte aligned"):
         # sizing the workspace needs shapes only, never the data pointers
         assert st2 == _lib.FA_OK
     else:
@@ -314,3 +324,20 @@ def test_decode_paged_limits(lib):
                                                k_stride=[16 * 8 * 128, 8 * 128, 128],
                                                v_stride=[16 * 8 * 128, 8 * 128, 128]))
     assert plain == paged
+
+
+def test_decode_fp8_strides_and_offsets(lib):
+    # FP8 codes are one byte: a stride of 16 elements is enough, 8 is not
+    base = dict(kv_format=1, k_scale=FAKE + 28672, v_scale=FAKE + 28800)
+    p = _decode(k_stride=[8192 * 8 * 128, 8 * 128 + 16, 128], **base)
+    assert _lib.decode_workspace_size(p)[0] == _lib.FA_OK
+    p = _decode(k_stride=[8192 * 8 * 128, 8 * 128 + 8, 128], **base)
+    assert _lib.decode_workspace_size(p)[0] == _lib.FA_ERR_UNSUPPORTED
+    # the 32-bit row offsets count bytes: 2^22 rows of 1 KiB codes fit, the same
+    # rows in bf16 would not
+    big = dict(batch=1, cache_capacity=1 << 22, k_stride=[(1 << 22) * 1024, 1024, 128],
+               v_stride=[(1 << 22) * 1024, 1024, 128])
+    assert _lib.decode_fwd(_decode(**big), FAKE, 1 << 40, 0) == _lib.FA_ERR_UNSUPPORTED
+    assert "4 GiB" in _lib.last_error()
+    st, n = _lib.decode_workspace_size(_decode(**big, **base))
+    assert st == _lib.FA_OK and n > 0

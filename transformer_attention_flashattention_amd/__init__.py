@@ -135,8 +135,33 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     return out, (lse if return_lse else None)
 
 
+def _kv_is_fp8(k_cache, v_cache, k_scale, v_scale) -> bool:
+    """FP8 E4M3 caches: torch.float8_e4m3fn tensors, or uint8 codes with scales."""
+    torch = _torch()
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    kinds = {t.dtype for t in (k_cache, v_cache)}
+    if kinds <= {fp8, torch.uint8} and len(kinds) == 1:
+        if k_scale is None or v_scale is None:
+            raise ValueError("FP8 E4M3 caches need k_scale and v_scale (one per KV head)")
+        return True
+    if k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale apply to FP8 E4M3 caches only")
+    return False
+
+
+def _kv_scales(x, Hkv, device):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        x = torch.tensor([float(x)] * Hkv if isinstance(x, (int, float)) else list(x),
+                         dtype=torch.float32)
+    x = x.to(device=device, dtype=torch.float32).contiguous()
+    if x.numel() != Hkv:
+        raise ValueError(f"k_scale / v_scale must have {Hkv} entries (one per KV head)")
+    return x
+
+
 def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys, al=None,
-                   table=None, capacity=None):
+                   table=None, capacity=None, scales=None):
     B, Hq, d = q.shape
     _, cap, Hkv, _ = k_cache.shape
     if table is not None:
@@ -165,6 +190,9 @@ def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys,
     if table is not None:
         p.block_table = table.data_ptr()
         p.page_size, p.pages_per_seq, p.num_pages = page_size, pages_per_seq, k_cache.shape[0]
+    if scales is not None:
+        p.kv_format = _lib.FA_KV_FP8_E4M3
+        p.k_scale, p.v_scale = scales[0].data_ptr(), scales[1].data_ptr()
     return p
 
 
@@ -181,14 +209,19 @@ def _block_table(table, B, device):
 
 
 def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
-                          chunk_keys: int = 0, block_table=None, capacity=None) -> int:
+                          chunk_keys: int = 0, block_table=None, capacity=None,
+                          k_scale=None, v_scale=None) -> int:
     """Workspace bytes ``decode`` needs for these shapes (host-only)."""
     table = block_table
     if table is not None and not isinstance(table, _torch().Tensor):
         table = _torch().tensor(table, dtype=_torch().int32)
     # sizing reads shapes only; the table's contents stay where they are
+    scales = None
+    if _kv_is_fp8(k_cache, v_cache, k_scale, v_scale):
+        Hkv = k_cache.shape[2]
+        scales = (_kv_scales(k_scale, Hkv, "cpu"), _kv_scales(v_scale, Hkv, "cpu"))
     p = _decode_params(q, k_cache, v_cache, None, None, None, scale, window, chunk_keys,
-                       table=table, capacity=capacity)
+                       table=table, capacity=capacity, scales=scales)
     st, n = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     return n
@@ -196,7 +229,8 @@ def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
 
 def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, window: int = -1,
            chunk_keys: int = 0, workspace=None, out=None, lse=None, return_lse: bool = True,
-           alibi_slopes=None, block_table=None, capacity: Optional[int] = None):
+           alibi_slopes=None, block_table=None, capacity: Optional[int] = None,
+           k_scale=None, v_scale=None):
     """Single-token decode over a KV cache, contiguous or paged.
 
     q: [B, Hq, d]; k_cache, v_cache: [B, capacity, Hkv, d]; seqlens_k: [B]
@@ -210,6 +244,11 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     page pools [num_pages, page_size, Hkv, d]; logical row j of sequence b is
     row j % page_size of page block_table[b, j // page_size].  ``capacity``
     (default pages_per_seq * page_size) caps the lengths.
+
+    FP8 cache: caches of dtype ``torch.float8_e4m3fn`` (or ``uint8`` codes)
+    hold OCP FP8 E4M3 values; ``k_scale`` and ``v_scale`` (one fp32 value per
+    KV head, or one float for all) give element = scale * E4M3(code).  q and
+    the output stay bf16.
     """
     torch = _torch()
     _require_gpu(q, k_cache, v_cache)
@@ -220,7 +259,8 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     table = _block_table(block_table, B, q.device)
     if (table is None and k_cache.shape[0] != B) or k_cache.shape[3] != d:
         raise ValueError("cache shape does not match q")
-    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+    fp8 = _kv_is_fp8(k_cache, v_cache, k_scale, v_scale)
+    if not fp8 and not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("q and the caches must share one dtype")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         if t.stride(-1) != 1:
@@ -232,8 +272,12 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     al = _slopes(alibi_slopes, Hq, dev)
+    scales = None
+    if fp8:
+        Hkv = k_cache.shape[2]
+        scales = (_kv_scales(k_scale, Hkv, dev), _kv_scales(v_scale, Hkv, dev))
     p = _decode_params(q, k_cache, v_cache, sk, out, lse if return_lse else None, scale, window,
-                       chunk_keys, al, table, capacity)
+                       chunk_keys, al, table, capacity, scales)
     st, need = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     if workspace is None:

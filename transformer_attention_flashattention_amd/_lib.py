@@ -22,6 +22,8 @@ FA_ERR_HIP = 4
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_KV_PLAIN = 0
+FA_KV_FP8_E4M3 = 1
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_prefill_fwd", "fa_decode_workspace_size", "fa_decode_fwd",
@@ -86,6 +88,10 @@ class DecodeParams(ctypes.Structure):
         ("pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int32),
         ("reserved1", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 

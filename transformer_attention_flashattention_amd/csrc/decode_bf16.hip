@@ -33,11 +33,13 @@
 #include "fa_internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace fa {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int NTHREADS = 256;
@@ -135,15 +137,33 @@ __device__ __forceinline__ void chunking(const DecodeArgs &a, int lo, int L, int
     len = n > 0 ? (((Lv + n - 1) / n + kDecodeChunkUnit - 1) / kDecodeChunkUnit) * kDecodeChunkUnit : 0;
 }
 
-__device__ __forceinline__ u32x4 load_nt(const char *base, unsigned off) {
-    return __builtin_nontemporal_load((const u32x4 *)(base + off));
+// A buffer the launch only reads, seen through the constant address space:
+// uniform loads from it become scalar loads whose waits the compiler tracks
+// itself (through a generic pointer they become flat loads, and waiting for
+// one of those also waits for every K/V load in flight).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T *read_only(const T *p) {
+    return (const __attribute__((address_space(4))) T *)p;
+}
+
+template <typename T = u32x4>
+__device__ __forceinline__ T load_nt(const char *base, unsigned off) {
+    return __builtin_nontemporal_load((const T *)(base + off));
+}
+
+// Two FP8 E4M3 codes (bytes 0-1 of w, or bytes 2-3 with HI) as a bf16 pair.
+// Every E4M3 value is exact in bf16, so this loses nothing.
+template <bool HI>
+__device__ __forceinline__ unsigned e4m3x2_to_bf16x2(unsigned w) {
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
 // a slice of it); ALIBI: add the per-head linear bias -m (L - 1 - j); PAGED:
-// the cache is a pool of pages named by a block table.  Chunk lengths are
-// multiples of NWAVES * KT.
-template <int D, int GT, bool ALIBI, bool PAGED>
+// the cache is a pool of pages named by a block table; KV8: K and V are FP8
+// E4M3 codes with one scale per KV head each.  Chunk lengths are multiples of
+// NWAVES * KT.
+template <int D, int GT, bool ALIBI, bool PAGED, bool KV8>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
     constexpr int SKP = 64 / SL;             // keys per score pass
@@ -213,21 +233,25 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // contiguous cache: the sequence's rows of this KV head (paged: the
     // pool's page 0, replaced per tile)
-    const char *Kp = (const char *)((const unsigned short *)a.k + (PAGED ? 0 : b * a.k_sb) + kvh * a.k_sh);
-    const char *Vp = (const char *)((const unsigned short *)a.v + (PAGED ? 0 : b * a.v_sb) + kvh * a.v_sh);
+    constexpr int ES = KV8 ? 1 : 2;                    // bytes per cached element
+    const char *Kp = (const char *)a.k + ((PAGED ? 0 : b * a.k_sb) + kvh * a.k_sh) * ES;
+    const char *Vp = (const char *)a.v + ((PAGED ? 0 : b * a.v_sb) + kvh * a.v_sh) * ES;
     // row offsets within one sequence (one page) fit 32 bits (checked on the host)
-    const unsigned k_row = (unsigned)a.k_ss * 2u, v_row = (unsigned)a.v_ss * 2u;
+    const unsigned k_row = (unsigned)a.k_ss * ES, v_row = (unsigned)a.v_ss * ES;
     const int s_key = lane / SL, s_sub = lane % SL;    // score layout
     const int v_key = lane / VL, v_sub = lane % VL;    // value layout
     const int my_g = s_sub < GT ? s_sub : 0;           // head whose P this lane produces
 
-    // query slice of every head, the same 16 dims a lane holds of each key:
-    // dims 8 s_sub .. +8 and D/2 + 8 s_sub .. +8 (8 bf16 pairs)
+    // query slice of every head, the same 16 dims a lane holds of each key
+    // (8 bf16 pairs): bf16 keys, dims 8 s_sub .. +8 and D/2 + 8 s_sub .. +8
+    // (each key load instruction then covers one contiguous half of every
+    // row); FP8 keys, dims 16 s_sub .. +16 (one 16-byte load per row piece)
     unsigned qr[GT][8];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-        const unsigned short *qp = (const unsigned short *)a.q + b * a.q_sb + (h0 + g) * a.q_sh + s_sub * 8;
-        const u32x4 x0 = *(const u32x4 *)qp, x1 = *(const u32x4 *)(qp + D / 2);
+        const unsigned short *qp = (const unsigned short *)a.q + b * a.q_sb + (h0 + g) * a.q_sh
+                                   + s_sub * (KV8 ? 16 : 8);
+        const u32x4 x0 = *(const u32x4 *)qp, x1 = *(const u32x4 *)(qp + (KV8 ? 8 : D / 2));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             qr[g][i] = x0[i];
@@ -249,9 +273,14 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     float alibi_raw[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) alibi_raw[g] = ALIBI ? -a.alibi[h0 + g] / a.scale : 0.f;
+    // FP8 cache: the per-KV-head scales (K's multiplies the raw dot product,
+    // V's the partial P.V)
+    const float k_scale = KV8 ? read_only(a.k_scale)[kvh] : 1.f;
+    const float v_scale = KV8 ? read_only(a.v_scale)[kvh] : 1.f;
 
-    // This wavefront's tiles t = 0 .. C/128 - 1 start at key base + 128 t; the
-    // ones holding a visible key form one contiguous range [ta, tb).
+    // This wavefront's tiles t = 0, 1, ... start at key base + STEP t (STEP =
+    // NWAVES * KT); the ones holding a visible key form one contiguous range
+    // [ta, tb).
     constexpr int STEP = NWAVES * KT;
     const int ntl = C / STEP;
     const int base = k0 + wave * KT;
@@ -270,41 +299,41 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     // the tile clamps to the same one.  That page is the page of the tile's
     // first key clamped to [jlo, jhi); the wavefront reads its table entry
     // (one uniform load) and addresses the rows inside it.
-    u32x4 kb[NBUF][SP][2], vb[NBUF][VP];
-    auto load = [&](int t, u32x4 (&kt)[SP][2], u32x4 (&vt)[VP]) __attribute__((always_inline)) {
+    // K: two 16-byte pieces per lane and pass (bf16) or one (FP8); V: 8 dims
+    // per lane, 16 bytes (bf16) or 8 bytes (FP8)
+    constexpr int KPC = KV8 ? 1 : 2;
+    using VVec = typename std::conditional<KV8, u32x2, u32x4>::type;
+    u32x4 kb[NBUF][SP][KPC];
+    VVec vb[NBUF][VP];
+    auto load = [&](int t, u32x4 (&kt)[SP][KPC], VVec (&vt)[VP]) __attribute__((always_inline)) {
         const int t0 = tile_key0(t);
         const char *kbase = Kp, *vbase = Vp;
         int row0 = 0;                                  // logical key of row 0 at kbase
         if constexpr (PAGED) {
             const int anchor = min(max(t0, jlo), jhi - 1);
             const int pg = anchor / a.page_size;
-            // the table is read-only for the whole launch: reading it through
-            // the constant address space gives a scalar load whose wait the
-            // compiler tracks itself (a generic pointer gives a flat load,
-            // which would also wait for every K/V load in flight)
-            const __attribute__((address_space(4))) int32_t *table =
-                (const __attribute__((address_space(4))) int32_t *)a.block_table;
-            int phys = table[(int64_t)b * a.pages_per_seq + pg];
+            int phys = read_only(a.block_table)[(int64_t)b * a.pages_per_seq + pg];
             phys = min(max(phys, 0), a.num_pages - 1);
-            kbase = Kp + (int64_t)phys * a.k_sb * 2;
-            vbase = Vp + (int64_t)phys * a.v_sb * 2;
+            kbase = Kp + (int64_t)phys * a.k_sb * ES;
+            vbase = Vp + (int64_t)phys * a.v_sb * ES;
             row0 = pg * a.page_size;
         }
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
             const int j = min(max(t0 + p * SKP + s_key, jlo), jhi - 1);
-            // each load instruction covers one contiguous half of every row it touches
+            // each load instruction covers one contiguous half of every row it
+            // touches (bf16) or whole rows (FP8)
             const unsigned off = (unsigned)(j - row0) * k_row + s_sub * 16;
             kt[p][0] = load_nt(kbase, off);
-            kt[p][1] = load_nt(kbase, off + D);
+            if constexpr (!KV8) kt[p][1] = load_nt(kbase, off + D);
         }
 #pragma unroll
         for (int p = 0; p < VP; ++p) {
             const int j = min(max(t0 + p * VKP + v_key, jlo), jhi - 1);
-            vt[p] = load_nt(vbase, (unsigned)(j - row0) * v_row + v_sub * 16);
+            vt[p] = load_nt<VVec>(vbase, (unsigned)(j - row0) * v_row + v_sub * 8 * ES);
         }
     };
-    auto compute = [&](int t, const u32x4 (&kt)[SP][2], const u32x4 (&vt)[VP]) __attribute__((always_inline)) {
+    auto compute = [&](int t, const u32x4 (&kt)[SP][KPC], const VVec (&vt)[VP]) __attribute__((always_inline)) {
         const int t0 = tile_key0(t);
         // scores of this lane's keys for every head
         float s[SP][GT];
@@ -312,14 +341,25 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         for (int p = 0; p < SP; ++p) {
             const int j = t0 + p * SKP + s_key;
             const bool ok = j >= jlo && j < jhi;
+            // this lane's 16 dims of the key as 8 bf16 pairs, in qr's order
+            unsigned kw[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (KV8) {
+                    kw[2 * i] = e4m3x2_to_bf16x2<false>(kt[p][0][i]);
+                    kw[2 * i + 1] = e4m3x2_to_bf16x2<true>(kt[p][0][i]);
+                } else {
+                    kw[i] = kt[p][0][i];
+                    kw[4 + i] = kt[p][KPC - 1][i];
+                }
+            }
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = dot2(kt[p][0][i], qr[g][i], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = dot2(kt[p][1][i], qr[g][4 + i], acc);
+                for (int i = 0; i < 8; ++i) acc = dot2(kw[i], qr[g][i], acc);
                 acc = group_sum<SL>(acc);
+                if constexpr (KV8) acc *= k_scale;
                 if constexpr (ALIBI) acc = __builtin_fmaf((float)(L - 1 - j), alibi_raw[g], acc);
                 s[p][g] = ok ? acc : -INFINITY;
             }
@@ -391,9 +431,25 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             unsigned pp[GT];
 #pragma unroll
             for (int g = 0; g < GT; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
+            // this lane's 8 dims of keys p and p + 1 as bf16 pairs
+            unsigned wa[4], wb[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if constexpr (KV8) {
+                    wa[2 * i] = e4m3x2_to_bf16x2<false>(vt[p][i]);
+                    wa[2 * i + 1] = e4m3x2_to_bf16x2<true>(vt[p][i]);
+                    wb[2 * i] = e4m3x2_to_bf16x2<false>(vt[p + 1][i]);
+                    wb[2 * i + 1] = e4m3x2_to_bf16x2<true>(vt[p + 1][i]);
+                } else {
+                    wa[2 * i] = vt[p][2 * i];
+                    wa[2 * i + 1] = vt[p][2 * i + 1];
+                    wb[2 * i] = vt[p + 1][2 * i];
+                    wb[2 * i + 1] = vt[p + 1][2 * i + 1];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const unsigned va = vt[p][i], vb = vt[p + 1][i];                 // dims 2i, 2i+1
+                const unsigned va = wa[i], vb = wb[i];                           // dims 2i, 2i+1
                 const unsigned even = __builtin_amdgcn_perm(vb, va, 0x05040100u);  // (va.lo, vb.lo)
                 const unsigned odd = __builtin_amdgcn_perm(vb, va, 0x07060302u);   // (va.hi, vb.hi)
 #pragma unroll
@@ -464,7 +520,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             lacc = __builtin_fmaf(wt, mml[w][g][1], lacc);
         }
         const int64_t row = ((int64_t)b * a.heads_q + h0 + g) * a.max_chunks + chunk;
-        a.ws_o[row * D + d] = acc;
+        a.ws_o[row * D + d] = KV8 ? acc * v_scale : acc;
         if (d == 0) {
             a.ws_ml[row * 2 + 0] = M;
             a.ws_ml[row * 2 + 1] = lacc;
@@ -540,10 +596,16 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
         a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Lsum)) * LN2 : -INFINITY;
 }
 
+template <int D, int GT, bool ALIBI, bool PAGED>
+void launch_split_kv(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+    if (a.kv_fp8) hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true>), grid, dim3(NTHREADS), 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, false>), grid, dim3(NTHREADS), 0, s, a);
+}
+
 template <int D, int GT, bool ALIBI>
 void launch_split_paged(const DecodeArgs &a, dim3 grid, hipStream_t s) {
-    if (a.block_table) hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, true>), grid, dim3(NTHREADS), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, false>), grid, dim3(NTHREADS), 0, s, a);
+    if (a.block_table) launch_split_kv<D, GT, ALIBI, true>(a, grid, s);
+    else launch_split_kv<D, GT, ALIBI, false>(a, grid, s);
 }
 
 template <int D, int GT>

@@ -97,8 +97,12 @@ fa_status validate_decode(const fa_decode_params *p) {
         (p->chunk_keys < 0 || p->chunk_keys % fa::kDecodeChunkUnit != 0 || p->chunk_keys > 65536))
         return fail(FA_ERR_UNSUPPORTED, "chunk_keys must be 0 or a multiple of %d up to 65536 (got %d)",
                     fa::kDecodeChunkUnit, p->chunk_keys);
-    if (p->reserved0 != 0 || p->reserved1 != 0)
-        return fail(FA_ERR_INVALID_ARG, "reserved0 and reserved1 must be 0");
+    if (p->reserved0 != 0 || p->reserved1 != 0 || p->reserved2 != 0)
+        return fail(FA_ERR_INVALID_ARG, "reserved0, reserved1 and reserved2 must be 0");
+    if (p->kv_format != FA_KV_PLAIN && p->kv_format != FA_KV_FP8_E4M3)
+        return fail(FA_ERR_INVALID_ARG, "unknown kv_format %d", p->kv_format);
+    if (p->kv_format == FA_KV_PLAIN && (p->k_scale || p->v_scale))
+        return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be NULL with FA_KV_PLAIN");
     if (p->block_table) {
         if (p->page_size < fa::kDecodePageUnit || p->page_size > 65536 ||
             p->page_size % fa::kDecodePageUnit != 0)
@@ -116,8 +120,10 @@ fa_status validate_decode(const fa_decode_params *p) {
     }
     FA_TRY(check_scale(p->softmax_scale));
     FA_TRY(check_strides("q", p->q_stride, 2, 8));
-    FA_TRY(check_strides("k", p->k_stride, 3, 8));
-    FA_TRY(check_strides("v", p->v_stride, 3, 8));
+    // 16-byte vector access: 8 bf16 elements, or 16 FP8 codes
+    const int kv_vec = p->kv_format == FA_KV_FP8_E4M3 ? 16 : 8;
+    FA_TRY(check_strides("k", p->k_stride, 3, kv_vec));
+    FA_TRY(check_strides("v", p->v_stride, 3, kv_vec));
     FA_TRY(check_strides("o", p->o_stride, 2, 1));
     return FA_OK;
 }
@@ -133,6 +139,13 @@ fa_status validate_decode_pointers(const fa_decode_params *p) {
         return fail(FA_ERR_INVALID_ARG, "o must be 2-byte aligned");
     if ((reinterpret_cast<uintptr_t>(p->block_table) & 3u) != 0)
         return fail(FA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    if (p->kv_format == FA_KV_FP8_E4M3) {
+        if (!p->k_scale || !p->v_scale)
+            return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be non-NULL with FA_KV_FP8_E4M3");
+        if ((reinterpret_cast<uintptr_t>(p->k_scale) & 3u) != 0 ||
+            (reinterpret_cast<uintptr_t>(p->v_scale) & 3u) != 0)
+            return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+    }
     return FA_OK;
 }
 
@@ -245,7 +258,8 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     // the split kernel addresses the rows of one sequence (one page when
     // paged) with 32-bit byte offsets
     const int64_t rows_addressed = p->block_table ? p->page_size : p->cache_capacity;
-    if (rows_addressed * std::max(p->k_stride[1], p->v_stride[1]) * 2 > 0xffffffffLL)
+    const int64_t elem_bytes = p->kv_format == FA_KV_FP8_E4M3 ? 1 : 2;
+    if (rows_addressed * std::max(p->k_stride[1], p->v_stride[1]) * elem_bytes > 0xffffffffLL)
         return fail(FA_ERR_UNSUPPORTED, p->block_table ? "page_size x seq stride exceeds 4 GiB per page"
                                                        : "cache_capacity x seq stride exceeds 4 GiB per sequence");
     if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL ||
@@ -267,6 +281,8 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     a.alibi = p->alibi_slopes;
     a.block_table = p->block_table;
     a.page_size = p->page_size; a.pages_per_seq = p->pages_per_seq; a.num_pages = p->num_pages;
+    a.kv_fp8 = p->kv_format == FA_KV_FP8_E4M3;
+    a.k_scale = p->k_scale; a.v_scale = p->v_scale;
     const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
     const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = static_cast<float *>(workspace);

@@ -47,6 +47,8 @@ struct DecodeArgs {
     float scale;                   // softmax_scale
     const int32_t *block_table;    // paged cache: [batch, pages_per_seq], or null (contiguous)
     int32_t page_size, pages_per_seq, num_pages;
+    int32_t kv_fp8;                // 1: K/V are FP8 E4M3 codes scaled by k_scale / v_scale
+    const float *k_scale, *v_scale;  // [heads_kv] (FP8 cache)
 };
 
 // Each launcher enqueues its kernel(s) and returns the launch status.
