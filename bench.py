@@ -13,8 +13,9 @@ library), so the per-call averages are kernel time plus launch gaps.
 
 After the timed steps, the same two calls are timed with ALiBi slopes
 (reported under "alibi"), and the decode call over the same logical cache
-held in a paged pool of 16-row pages in shuffled order (reported under
-"paged"); neither is part of the step.
+held in a paged pool of 16-row pages in shuffled order (under "paged") and
+as FP8 E4M3 codes with per-KV-head scales (under "fp8_kv"); none of these is
+part of the step.
 
 Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
 algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
@@ -43,8 +44,8 @@ def prefill_flops(B, H, N, d):
     return 4.0 * d * H * B * N * (N + 1) / 2.0
 
 
-def decode_bytes(seqlens, Hq, Hkv, d, elt=2):
-    kv = float(np.sum(seqlens)) * Hkv * d * elt * 2
+def decode_bytes(seqlens, Hq, Hkv, d, elt=2, kv_elt=None):
+    kv = float(np.sum(seqlens)) * Hkv * d * (elt if kv_elt is None else kv_elt) * 2
     q_o = 2.0 * len(seqlens) * Hq * d * elt
     return kv + q_o + len(seqlens) * Hq * 4 + len(seqlens) * 4
 
@@ -234,6 +235,31 @@ def main():
     torch.cuda.synchronize()
     dec_p = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_p]))
     table_bytes = 4 * int(sum(-(-int(L) // page) for L in pp.seqlens_k))
+    del qp, kp, vp, tab
+
+    # the decode over an FP8 E4M3 cache of the same draws (per-KV-head scales)
+    fp = workloads.make_workload_fp8(5)
+    assert np.array_equal(fp.seqlens_k, dp.seqlens_k)
+    k8 = torch.from_numpy(fp.k_cache).to(dev).view(torch.float8_e4m3fn)
+    v8 = torch.from_numpy(fp.v_cache).to(dev).view(torch.float8_e4m3fn)
+    ks8 = torch.from_numpy(fp.k_scale).to(dev)
+    vs8 = torch.from_numpy(fp.v_scale).to(dev)
+    ws8 = torch.empty(fa.decode_workspace_size(qd, k8, v8, chunk_keys=args.decode_chunk,
+                                               k_scale=ks8, v_scale=vs8), dtype=torch.uint8,
+                      device=dev)
+    fa.decode(qd, k8, v8, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws8,
+              chunk_keys=args.decode_chunk, k_scale=ks8, v_scale=vs8)
+    torch.cuda.synchronize()
+    ev_f = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_alibi)]
+    for e in ev_f:
+        e[0].record()
+        fa.decode(qd, k8, v8, sk, scale=dp.scale, out=od, lse=lsed, workspace=ws8,
+                  chunk_keys=args.decode_chunk, k_scale=ks8, v_scale=vs8)
+        e[1].record()
+    torch.cuda.synchronize()
+    dec_f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_f]))
+    fp8_bytes = decode_bytes(dp.seqlens_k, Hq, Hkv, dd, kv_elt=1) + 2 * 4 * Hkv
+    del k8, v8
 
     pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
@@ -278,6 +304,11 @@ def main():
                   "decode_ms_mean": round(dec_a, 4),
                   "decode_gbs": round(dbytes / (dec_a * 1e-3) / 1e9, 1),
                   "calls": n_alibi},
+        "fp8_kv": {"format": "e4m3", "decode_ms_mean": round(dec_f, 4),
+                   "decode_gbs": round(fp8_bytes / (dec_f * 1e-3) / 1e9, 1),
+                   "frac_of_hbm_peak": round(fp8_bytes / (dec_f * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                   "speedup_vs_bf16_cache": round(float(dec_ms.mean()) / dec_f, 3),
+                   "algorithmic_bytes": fp8_bytes, "calls": n_alibi},
         "paged": {"page_size": page, "num_pages": int(pp.k_pool.shape[0]),
                   "decode_ms_mean": round(dec_p, 4),
                   "decode_gbs": round((dbytes + table_bytes) / (dec_p * 1e-3) / 1e9, 1),

@@ -80,10 +80,12 @@ def test_fp8_window_and_alibi(W):
     _case(dp, f"FP8 window {W} ALiBi", alibi_slopes=np.linspace(0.02, 0.2, 8).astype(np.float32))
 
 
-@pytest.mark.parametrize("page", [16, 48, 256])
+@pytest.mark.parametrize("page", [16, 48, 64, 256])
 def test_fp8_paged(page):
+    # 16- and 48-row pages take 16-key tiles, 64 and 256 take 32-key tiles
     pp = workloads.make_decode_paged(73, 9, 8, 2, 128, 1100, (1, 1100), page, "bf16",
-                                     window_left=-1 if page != 48 else 70, kv_dtype="fp8_e4m3")
+                                     window_left=70 if page in (48, 64) else -1,
+                                     kv_dtype="fp8_e4m3")
     say(f"[fp8] paged page={page} W={pp.window_left}")
     o, lse = run_decode_paged_fp8(pp)
     ro, rl = oracle_decode_paged_fp8(pp)

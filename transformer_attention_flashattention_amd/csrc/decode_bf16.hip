@@ -44,13 +44,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
-#ifndef DECODE_KT
-#define DECODE_KT 16
-#endif
 #ifndef DECODE_NBUF
 #define DECODE_NBUF 2
 #endif
-constexpr int KT = DECODE_KT;                // keys per wavefront tile
 constexpr int NBUF = DECODE_NBUF;            // tiles held in registers: 1 computing, NBUF-1 in flight
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;    // log2 of the largest un-rescaled p
@@ -120,10 +116,11 @@ __device__ __forceinline__ void visible_range(const DecodeArgs &a, int b, int &l
     lo = (a.window_left > 0) ? max(0, L - a.window_left) : 0;
 }
 
-// First key of the chunk grid: lo itself, or for a paged cache lo rounded
-// down to a whole tile, so that every tile lies inside one page.
+// First key of the chunk grid: lo rounded down to a multiple of a.origin_align (1 for a
+// contiguous cache; the tile length for a paged cache, so that every tile
+// lies inside one page).  Both kernels of a call use the same value.
 __device__ __forceinline__ int chunk_origin(const DecodeArgs &a, int lo) {
-    return a.block_table ? (lo & ~(KT - 1)) : lo;
+    return lo & ~(a.origin_align - 1);            // origin_align: 1, 16 or 32
 }
 
 // The keys [origin, L) of a sequence are cut into n = ceil((L - origin) /
@@ -162,8 +159,8 @@ __device__ __forceinline__ unsigned e4m3x2_to_bf16x2(unsigned w) {
 // a slice of it); ALIBI: add the per-head linear bias -m (L - 1 - j); PAGED:
 // the cache is a pool of pages named by a block table; KV8: K and V are FP8
 // E4M3 codes with one scale per KV head each.  Chunk lengths are multiples of
-// NWAVES * KT.
-template <int D, int GT, bool ALIBI, bool PAGED, bool KV8>
+// NWAVES * KT.  KT: keys per wavefront tile.
+template <int D, int GT, bool ALIBI, bool PAGED, bool KV8, int KT>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
     constexpr int SKP = 64 / SL;             // keys per score pass
@@ -596,10 +593,20 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
         a.lse[(int64_t)b * a.heads_q + h] = ok ? (M_use + log2f(Lsum)) * LN2 : -INFINITY;
 }
 
+// Tile length: 16 keys, or 32 for an FP8 cache (the same bytes per tile as
+// bf16, so as many bytes in flight per wavefront) when pages allow it.
+int tile_keys(const DecodeArgs &a) {
+    return (a.kv_fp8 && (!a.block_table || a.page_size % 32 == 0)) ? 32 : 16;
+}
+
 template <int D, int GT, bool ALIBI, bool PAGED>
 void launch_split_kv(const DecodeArgs &a, dim3 grid, hipStream_t s) {
-    if (a.kv_fp8) hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true>), grid, dim3(NTHREADS), 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, false>), grid, dim3(NTHREADS), 0, s, a);
+    if (!a.kv_fp8)
+        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, false, 16>), grid, dim3(NTHREADS), 0, s, a);
+    else if (tile_keys(a) == 32)
+        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 32>), grid, dim3(NTHREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 16>), grid, dim3(NTHREADS), 0, s, a);
 }
 
 template <int D, int GT, bool ALIBI>
@@ -634,7 +641,9 @@ hipError_t launch_all(const DecodeArgs &a, int gt, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_wg, hipStream_t s) {
+hipError_t launch_decode_bf16(const DecodeArgs &args, int head_dim, int heads_per_wg, hipStream_t s) {
+    DecodeArgs a = args;
+    a.origin_align = a.block_table ? tile_keys(a) : 1;
     if (head_dim == 128) return launch_all<128>(a, heads_per_wg, s);
     return launch_all<64>(a, heads_per_wg, s);
 }

@@ -49,6 +49,7 @@ struct DecodeArgs {
     int32_t page_size, pages_per_seq, num_pages;
     int32_t kv_fp8;                // 1: K/V are FP8 E4M3 codes scaled by k_scale / v_scale
     const float *k_scale, *v_scale;  // [heads_kv] (FP8 cache)
+    int32_t origin_align;          // chunk grid origin alignment (set by the launcher)
 };
 
 // Each launcher enqueues its kernel(s) and returns the launch status.

@@ -342,7 +342,8 @@ def make_workload(idx: int):
                        w.pop("capacity"), w.pop("len_range"), w.pop("dtype"), **w)
 
 
-def make_workload_paged(idx: int, page_size: int) -> PagedDecodeProblem:
+def make_workload_paged(idx: int, page_size: int,
+                        kv_dtype: Optional[str] = None) -> PagedDecodeProblem:
     """A named decode workload with its cache in a paged pool (same logical
     rows as :func:`make_workload` for that index)."""
     w = dict(WORKLOADS[idx])
@@ -350,4 +351,16 @@ def make_workload_paged(idx: int, page_size: int) -> PagedDecodeProblem:
         raise ValueError("only decode workloads have a paged form")
     w.pop("name")
     return make_decode_paged(w.pop("seed"), w.pop("B"), w.pop("Hq"), w.pop("Hkv"), w.pop("d"),
-                             w.pop("capacity"), w.pop("len_range"), page_size, w.pop("dtype"), **w)
+                             w.pop("capacity"), w.pop("len_range"), page_size, w.pop("dtype"),
+                             kv_dtype=kv_dtype, **w)
+
+
+def make_workload_fp8(idx: int) -> DecodeProblem:
+    """A named decode workload with an FP8 E4M3 cache (same draws)."""
+    w = dict(WORKLOADS[idx])
+    if w.pop("kind") != "decode":
+        raise ValueError("only decode workloads have an FP8 cache")
+    w.pop("name")
+    return make_decode(w.pop("seed"), w.pop("B"), w.pop("Hq"), w.pop("Hkv"), w.pop("d"),
+                       w.pop("capacity"), w.pop("len_range"), w.pop("dtype"),
+                       kv_dtype="fp8_e4m3", **w)
