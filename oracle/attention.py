@@ -66,7 +66,17 @@ notes):
   bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 is NaN,
   largest finite value 448), with one fp32 scale per KV head for K and one
   for V; the element's value is ``scale * E4M3(code)``.  Attention over the
-  dequantized cache is the decode above, unchanged.
+  dequantized cache is the decode above, unchanged;
+* RoPE (the jsqmd.com page, section 三, rotary position encoding and its
+  fusion into attention): the vector at position m is rotated pair by pair,
+  each pair of adjacent dimensions (2p, 2p + 1) by its own angle; the page
+  gives no angle formula, so the angles enter as tables cos[m, p] and
+  sin[m, p] (float32), and only the first ``rotary_dim`` dimensions rotate
+  (the page's ``rotary_dim`` argument).  Rotation of (a, b) by an angle with
+  cosine c and sine s gives (a c - b s, a s + b c).  Positions follow the
+  causal alignment: key j sits at position j and query row i at
+  ``i + Lk - Lq``.  Q and K are rotated first; attention over the rotated
+  vectors is unchanged.
 
 Every function here is pinned in ``tests/test_oracle.py`` against closed
 forms, brute force on tiny integer inputs, library routines and invariants.
@@ -113,6 +123,24 @@ def alibi_bias(rows: np.ndarray, Nk: int, Lq: int, Lk: int, slope: float) -> np.
     return -float(slope) * np.abs(pos - j).astype(np.float64)
 
 
+def rope_rotate(x: np.ndarray, positions, cos_table, sin_table, rotary_dim: int) -> np.ndarray:
+    """Rotate rows ``x[n, :]`` (float64 copy) at ``positions[n]``: for every
+    pair p < rotary_dim / 2, (x[2p], x[2p+1]) -> (x[2p] c - x[2p+1] s,
+    x[2p] s + x[2p+1] c) with c = cos_table[pos, p], s = sin_table[pos, p]."""
+    x = np.array(x, dtype=np.float64)
+    if rotary_dim % 2 or rotary_dim > x.shape[-1]:
+        raise ValueError("rotary_dim must be even and at most the row length")
+    pos = np.asarray(positions, dtype=np.int64)
+    half = rotary_dim // 2
+    c = np.asarray(cos_table, dtype=np.float32)[pos][:, :half].astype(np.float64)
+    s = np.asarray(sin_table, dtype=np.float32)[pos][:, :half].astype(np.float64)
+    a = x[:, 0:rotary_dim:2].copy()
+    b = x[:, 1:rotary_dim:2].copy()
+    x[:, 0:rotary_dim:2] = a * c - b * s
+    x[:, 1:rotary_dim:2] = a * s + b * c
+    return x
+
+
 def _attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                  vis: np.ndarray, bias: Optional[np.ndarray] = None):
     """Three-step attention for one (batch, head): q_rows [r, d], k/v [Nk, d]."""
@@ -145,7 +173,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
               seqlens_k: Optional[Sequence[int]] = None,
               rows: Optional[Sequence[int]] = None,
               heads: Optional[Sequence[int]] = None,
-              alibi_slopes: Optional[Sequence[float]] = None):
+              alibi_slopes: Optional[Sequence[float]] = None,
+              rope: Optional[tuple] = None):
     """Reference attention forward.
 
     q: [B, Nq, Hq, d], k and v: [B, Nk, Hkv, d] (any real dtype; used as
@@ -155,6 +184,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     subset of query rows / heads; each output row depends only on its own
     query and visible keys, so a subset is exact.  ``alibi_slopes`` (one
     float32 value per query head, or None) adds the ALiBi bias to the scores.
+    ``rope = (cos_table, sin_table, rotary_dim)`` rotates Q rows (at
+    ``i + Lk - Lq``) and K rows (at ``j``) before the scores; only rows
+    inside the valid lengths are rotated (the others are never visible).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -179,11 +211,21 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
         Lq = Nq if seqlens_q is None else int(seqlens_q[b])
         Lk = Nk if seqlens_k is None else int(seqlens_k[b])
         vis = visible_matrix(rows, Nk, Lq, Lk, causal, window_left)
+        if rope is not None:
+            cos_t, sin_t, rdim = rope
+            q_ok = np.flatnonzero(rows < Lq)          # rows inside the valid length
+            k_ok = np.arange(min(Lk, Nk))
         for hi, h in enumerate(heads):
             kvh = h // group
             bias = None if alibi_slopes is None else alibi_bias(rows, Nk, Lq, Lk, slopes[h])
-            ob, lb = _attend_rows(q[b, rows, h, :], k[b, :, kvh, :], v[b, :, kvh, :],
-                                  scale, vis, bias)
+            qb, kb = q[b, rows, h, :], k[b, :, kvh, :]
+            if rope is not None:
+                qb, kb = qb.copy(), kb.copy()
+                if len(q_ok):
+                    qb[q_ok] = rope_rotate(qb[q_ok], rows[q_ok] + (Lk - Lq), cos_t, sin_t, rdim)
+                if len(k_ok):
+                    kb[k_ok] = rope_rotate(kb[k_ok], k_ok, cos_t, sin_t, rdim)
+            ob, lb = _attend_rows(qb, kb, v[b, :, kvh, :], scale, vis, bias)
             o[b, :, hi, :] = ob
             lse[b, hi, :] = lb
     return o, lse
@@ -192,7 +234,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
 def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
            seqlens_k: Sequence[int], *, scale: float, window_left: int = -1,
            batches: Optional[Sequence[int]] = None,
-           alibi_slopes: Optional[Sequence[float]] = None):
+           alibi_slopes: Optional[Sequence[float]] = None,
+           rope_q: Optional[tuple] = None):
     """Reference single-token decode over a contiguous BSHD cache.
 
     q: [B, Hq, d]; caches: [B, capacity, Hkv, d]; seqlens_k: [B] (clamped to
@@ -200,6 +243,9 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     sees cache rows 0 .. L_b - 1 (restricted by the window if W >= 1).
     Returns O: [B', Hq, d] and LSE: [B', Hq] in float64.  Only the valid
     prefix of each cache is read, so poisoned rows beyond it never matter.
+    ``rope_q = (cos_table, sin_table, rotary_dim)`` rotates the query at its
+    position L_b - 1; cached keys are taken as stored (a decode cache holds
+    keys already rotated at their own positions when they were appended).
     """
     B, Hq, d = q.shape
     cap = k_cache.shape[1]
@@ -209,7 +255,10 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     lse = np.zeros((len(batches), Hq), dtype=np.float64)
     for bi, b in enumerate(batches):
         L = int(min(max(int(seqlens_k[b]), 0), cap))
-        ob, lb = attention(q[b][None, None], k_cache[b, :L][None], v_cache[b, :L][None],
+        qb = q[b]
+        if rope_q is not None and L > 0:
+            qb = rope_rotate(qb, np.full(qb.shape[0], L - 1), *rope_q)
+        ob, lb = attention(qb[None, None], k_cache[b, :L][None], v_cache[b, :L][None],
                            scale=scale, causal=True, window_left=window_left,
                            seqlens_q=[1], seqlens_k=[L], alibi_slopes=alibi_slopes)
         o[bi] = ob[0, 0]

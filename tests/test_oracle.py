@@ -697,3 +697,94 @@ def test_fp8_generator_codes_round_to_nearest():
         assert np.all(np.abs(vals - y) <= 0.5 * step * (1 + 1e-6))
         for h in range(2):
             assert np.abs(vals[:, :, h]).max() == 448.0
+
+
+# ---------------------------------------------------------------------------
+# RoPE: pair rotation and its use in attention
+# ---------------------------------------------------------------------------
+def _angle_tables(n_pos, half, base=10000.0, dtype=np.float32):
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / (2 * half))
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(dtype), np.sin(ang).astype(dtype)
+
+
+def test_rope_literal_rotation():
+    # pair 0 turned by 90 degrees, pair 1 by 180 degrees (exact table values)
+    cos_t = np.array([[0.0, -1.0]], np.float32)
+    sin_t = np.array([[1.0, 0.0]], np.float32)
+    out = oracle.rope_rotate(np.array([[1.0, 0.0, 0.0, 1.0]]), [0], cos_t, sin_t, 4)
+    assert out.tolist() == [[0.0, 1.0, 0.0, -1.0]]
+    # rotary_dim 2 leaves the second pair alone
+    out = oracle.rope_rotate(np.array([[1.0, 0.0, 0.0, 1.0]]), [0], cos_t, sin_t, 2)
+    assert out.tolist() == [[0.0, 1.0, 0.0, 1.0]]
+
+
+def test_rope_matches_complex_multiplication_and_keeps_pair_norms():
+    rng = np.random.default_rng(7)
+    cos_t, sin_t = _angle_tables(50, 8)
+    x = rng.standard_normal((20, 24))
+    pos = rng.integers(0, 50, 20)
+    out = oracle.rope_rotate(x, pos, cos_t, sin_t, 16)
+    z = (x[:, 0:16:2] + 1j * x[:, 1:16:2]) * (cos_t[pos].astype(np.float64) + 1j * sin_t[pos].astype(np.float64))
+    np.testing.assert_allclose(out[:, 0:16:2], z.real, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out[:, 1:16:2], z.imag, rtol=0, atol=1e-14)
+    assert np.array_equal(out[:, 16:], x[:, 16:])
+    n_in = x[:, 0:16:2] ** 2 + x[:, 1:16:2] ** 2
+    n_out = out[:, 0:16:2] ** 2 + out[:, 1:16:2] ** 2
+    c64, s64 = cos_t[pos].astype(np.float64), sin_t[pos].astype(np.float64)
+    np.testing.assert_allclose(n_out, n_in * (c64 ** 2 + s64 ** 2), rtol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position():
+    """With angles proportional to the position, q at m against k at n gives
+    the same product as q at m + t against k at n + t (to the float32
+    rounding of the table entries, which the oracle reads as float32)."""
+    rng = np.random.default_rng(8)
+    cos_t, sin_t = _angle_tables(400, 16)
+    q, k = rng.standard_normal((1, 32)), rng.standard_normal((1, 32))
+    for m, n, t in ((5, 3, 100), (0, 0, 399), (250, 10, 37)):
+        a = oracle.rope_rotate(q, [m], cos_t, sin_t, 32) @ oracle.rope_rotate(k, [n], cos_t, sin_t, 32).T
+        b = oracle.rope_rotate(q, [m + t], cos_t, sin_t, 32) @ oracle.rope_rotate(k, [n + t], cos_t, sin_t, 32).T
+        assert abs(a - b) < 2e-6 * (1 + abs(a))
+
+
+def test_rope_attention_query_alignment():
+    """The last M query rows of an N-row causal problem are the same rows as a
+    problem holding only those M queries against the same N keys (query row
+    i sits at position i + Lk - Lq), so RoPE must give them the same output."""
+    p = workloads.make_prefill(80, 1, 40, 40, 2, 1, 16, "f32", causal=True)
+    q, k, v = _f64(p)
+    cos_t, sin_t = _angle_tables(40, 6)
+    rope = (cos_t, sin_t, 12)
+    o_full, l_full = oracle.attention(q, k, v, scale=0.3, causal=True, rope=rope)
+    o_tail, l_tail = oracle.attention(q[:, 30:], k, v, scale=0.3, causal=True, rope=rope)
+    np.testing.assert_allclose(o_tail, o_full[:, 30:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_tail, l_full[:, :, 30:], rtol=0, atol=1e-13)
+    # and rotation really changes the result (it is not a no-op)
+    o_plain, _ = oracle.attention(q, k, v, scale=0.3, causal=True)
+    assert np.abs(o_plain - o_full).max() > 1e-3
+
+
+def test_rope_decode_query_at_last_position():
+    """Decode rotates the query at L - 1 and reads keys as stored: against
+    keys rotated at their positions, it equals one-row causal attention with
+    RoPE on both sides."""
+    dp = workloads.make_decode(81, 3, 4, 2, 16, 30, (1, 30), "f32",
+                               lengths=np.array([30, 7, 1], dtype=np.int32))
+    q = workloads.to_f64(dp.q, "f32")
+    kc = workloads.to_f64(dp.k_cache, "f32")
+    vc = workloads.to_f64(dp.v_cache, "f32")
+    cos_t, sin_t = _angle_tables(30, 8)
+    rope = (cos_t, sin_t, 16)
+    k_rot = kc.copy()
+    for b in range(3):
+        L = int(dp.seqlens_k[b])
+        for h in range(2):
+            k_rot[b, :L, h] = oracle.rope_rotate(kc[b, :L, h], np.arange(L), *rope)
+    o, l = oracle.decode(q, k_rot, vc, dp.seqlens_k, scale=0.25, rope_q=rope)
+    for b in range(3):
+        L = int(dp.seqlens_k[b])
+        ro, rl = oracle.attention(q[b][None, None], kc[b, :L][None], vc[b, :L][None], scale=0.25,
+                                  causal=True, rope=rope)
+        np.testing.assert_allclose(o[b], ro[0, 0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l[b], rl[0, :, 0], rtol=0, atol=1e-13)
