@@ -101,6 +101,25 @@ typedef enum {
  * the bias generated in the kernel (no bias matrix in memory).  The slopes
  * are read on the device, so their values are not validated; NULL = none.
  *
+ * RoPE (jsqmd.com page, section 三, rotary position encoding fused into
+ * attention): with rotary_dim > 0, every pair of adjacent dims (2p, 2p + 1),
+ * p < rotary_dim / 2, of a query or key vector at position m is rotated:
+ * (x, y) -> (x c - y s, x s + y c), c = rope_cos[m * rotary_dim / 2 + p],
+ * s = rope_sin[...] (device fp32 tables [rope_max_pos, rotary_dim / 2]; the
+ * page gives no angle formula, so the caller supplies the tables).  Key j
+ * sits at position j, query row i at i + (Lk - Lq).  The rotated vectors are
+ * rounded to the input dtype before the products, as a separate rotation
+ * pass would store them.  Queries are rotated in registers as they are
+ * loaded.  Keys: the fp32 path rotates each key tile as it is staged; the
+ * bf16 path first rotates K once into `workspace` (a copy of K's valid rows,
+ * contiguous [batch, seqlen_k, heads_kv, head_dim]), since its kernel reads
+ * every key tile once per 256 query rows and a rotation at each read would
+ * cost the matrix wavefronts that many times the vector work.  Requirements:
+ * rotary_dim a multiple of 8 and at most head_dim; rope_max_pos >= seqlen_k;
+ * tables 16-byte aligned; for bf16, workspace (16-byte aligned, caller-owned,
+ * scratch after the call) of at least fa_prefill_workspace_size() bytes.
+ * With rotary_dim = 0 the tables and the workspace are ignored.
+ *
  * Requirements: head_dim in {64, 128}; heads_q % heads_kv == 0;
  * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
  * window_left == -1 or >= 1; extents >= 0; seqlens arrays (if given) are
@@ -133,6 +152,12 @@ typedef struct {
     int64_t v_stride[3];
     int64_t o_stride[3];
     const float *alibi_slopes;           /* device fp32 [heads_q] or NULL        */
+    const float *rope_cos;               /* device fp32 [rope_max_pos, rotary_dim/2] */
+    const float *rope_sin;               /* same shape                           */
+    int32_t rotary_dim;                  /* 0 = no RoPE, else k * 8 <= head_dim  */
+    int32_t rope_max_pos;                /* rows of the tables (>= seqlen_k)     */
+    void *workspace;                     /* bf16 RoPE only: rotated K            */
+    int64_t workspace_bytes;
 } fa_prefill_params;
 
 /*
@@ -195,6 +220,11 @@ typedef struct {
  * must be multiples of 16.  Works with the contiguous and the paged layout.
  * With FA_KV_PLAIN, k_scale and v_scale must be NULL.
  *
+ * RoPE (as for prefill): with rotary_dim > 0 the query is rotated at its
+ * position L_b - 1 as it is loaded.  Cached keys are read as stored: a
+ * decode cache holds keys already rotated at their own positions, written
+ * when each token was appended.  rope_max_pos >= cache_capacity.
+ *
  * Requirements: dtype FA_DTYPE_BF16; head_dim in {64, 128};
  * heads_q % heads_kv == 0; cache_capacity >= 1; softmax_scale finite and > 0.
  */
@@ -229,11 +259,20 @@ typedef struct {
     int32_t reserved2;                   /* must be 0                            */
     const float *k_scale;                /* device fp32 [heads_kv] (FP8) or NULL */
     const float *v_scale;                /* device fp32 [heads_kv] (FP8) or NULL */
+    const float *rope_cos;               /* device fp32 [rope_max_pos, rotary_dim/2] */
+    const float *rope_sin;               /* same shape                           */
+    int32_t rotary_dim;                  /* 0 = no RoPE, else k * 8 <= head_dim  */
+    int32_t rope_max_pos;                /* rows of the tables (>= capacity)     */
 } fa_decode_params;
 
 /* Enqueue the prefill forward pass.  Returns FA_OK, FA_ERR_INVALID_ARG,
  * FA_ERR_UNSUPPORTED or FA_ERR_HIP (launch failure). */
 fa_status fa_prefill_fwd(const fa_prefill_params *params, void *hip_stream);
+
+/* Bytes of device workspace fa_prefill_fwd needs for `params` (host-only; 0
+ * unless bf16 with RoPE, then batch * seqlen_k * heads_kv * head_dim * 2).
+ * Writes *bytes and returns FA_OK, or returns an argument error. */
+fa_status fa_prefill_workspace_size(const fa_prefill_params *params, size_t *bytes);
 
 /* Bytes of device workspace fa_decode_fwd needs for `params` (host-only
  * computation; no HIP call).  Writes *bytes and returns FA_OK, or returns an
@@ -256,7 +295,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10300
+#define FA_ABI_VERSION 10400
 
 #ifdef __cplusplus
 }

@@ -6,4 +6,5 @@ leg may import anything under ``oracle/``.  The library's product path
 the two share no code.
 """
 from .attention import (alibi_bias, attention, decode, decode_paged, dequantize_kv,  # noqa: F401
-                        fp8_e4m3_value, gather_paged, rope_rotate, visible, visible_matrix)
+                        fp8_e4m3_value, gather_paged, rope_rotate, round_to_dtype, visible,
+                        visible_matrix)

@@ -75,8 +75,10 @@ notes):
   (the page's ``rotary_dim`` argument).  Rotation of (a, b) by an angle with
   cosine c and sine s gives (a c - b s, a s + b c).  Positions follow the
   causal alignment: key j sits at position j and query row i at
-  ``i + Lk - Lq``.  Q and K are rotated first; attention over the rotated
-  vectors is unchanged.
+  ``i + Lk - Lq``.  Q and K are rotated first and, as the page's separate
+  form (apply_rope, then flash_attention) stores them, held in the input
+  dtype: each rotated element is rounded to nearest even in bf16 (or fp32).
+  Attention over the rotated vectors is unchanged.
 
 Every function here is pinned in ``tests/test_oracle.py`` against closed
 forms, brute force on tiny integer inputs, library routines and invariants.
@@ -123,7 +125,23 @@ def alibi_bias(rows: np.ndarray, Nk: int, Lq: int, Lk: int, slope: float) -> np.
     return -float(slope) * np.abs(pos - j).astype(np.float64)
 
 
-def rope_rotate(x: np.ndarray, positions, cos_table, sin_table, rotary_dim: int) -> np.ndarray:
+def round_to_dtype(x: np.ndarray, dtype: Optional[str]) -> np.ndarray:
+    """Round float64 values to the nearest bf16 or fp32 value (ties to even),
+    returned as float64; ``dtype=None`` leaves them unrounded.  bf16: the
+    significand is scaled to 8 bits and rounded by ``rint`` (half to even)."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype is None:
+        return x.copy()
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    m, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def rope_rotate(x: np.ndarray, positions, cos_table, sin_table, rotary_dim: int,
+                store: Optional[str] = None) -> np.ndarray:
     """Rotate rows ``x[n, :]`` (float64 copy) at ``positions[n]``: for every
     pair p < rotary_dim / 2, (x[2p], x[2p+1]) -> (x[2p] c - x[2p+1] s,
     x[2p] s + x[2p+1] c) with c = cos_table[pos, p], s = sin_table[pos, p]."""
@@ -136,8 +154,8 @@ def rope_rotate(x: np.ndarray, positions, cos_table, sin_table, rotary_dim: int)
     s = np.asarray(sin_table, dtype=np.float32)[pos][:, :half].astype(np.float64)
     a = x[:, 0:rotary_dim:2].copy()
     b = x[:, 1:rotary_dim:2].copy()
-    x[:, 0:rotary_dim:2] = a * c - b * s
-    x[:, 1:rotary_dim:2] = a * s + b * c
+    x[:, 0:rotary_dim:2] = round_to_dtype(a * c - b * s, store)
+    x[:, 1:rotary_dim:2] = round_to_dtype(a * s + b * c, store)
     return x
 
 
@@ -184,8 +202,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     subset of query rows / heads; each output row depends only on its own
     query and visible keys, so a subset is exact.  ``alibi_slopes`` (one
     float32 value per query head, or None) adds the ALiBi bias to the scores.
-    ``rope = (cos_table, sin_table, rotary_dim)`` rotates Q rows (at
-    ``i + Lk - Lq``) and K rows (at ``j``) before the scores; only rows
+    ``rope = (cos_table, sin_table, rotary_dim[, store])`` rotates Q rows
+    (at ``i + Lk - Lq``) and K rows (at ``j``) before the scores, rounding
+    the rotated elements to ``store`` ("bf16", "f32" or None); only rows
     inside the valid lengths are rotated (the others are never visible).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -212,7 +231,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
         Lk = Nk if seqlens_k is None else int(seqlens_k[b])
         vis = visible_matrix(rows, Nk, Lq, Lk, causal, window_left)
         if rope is not None:
-            cos_t, sin_t, rdim = rope
+            cos_t, sin_t, rdim = rope[:3]
+            store = rope[3] if len(rope) > 3 else None
             q_ok = np.flatnonzero(rows < Lq)          # rows inside the valid length
             k_ok = np.arange(min(Lk, Nk))
         for hi, h in enumerate(heads):
@@ -222,9 +242,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
             if rope is not None:
                 qb, kb = qb.copy(), kb.copy()
                 if len(q_ok):
-                    qb[q_ok] = rope_rotate(qb[q_ok], rows[q_ok] + (Lk - Lq), cos_t, sin_t, rdim)
+                    qb[q_ok] = rope_rotate(qb[q_ok], rows[q_ok] + (Lk - Lq), cos_t, sin_t, rdim,
+                                           store)
                 if len(k_ok):
-                    kb[k_ok] = rope_rotate(kb[k_ok], k_ok, cos_t, sin_t, rdim)
+                    kb[k_ok] = rope_rotate(kb[k_ok], k_ok, cos_t, sin_t, rdim, store)
             ob, lb = _attend_rows(qb, kb, v[b, :, kvh, :], scale, vis, bias)
             o[b, :, hi, :] = ob
             lse[b, hi, :] = lb
@@ -243,8 +264,8 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     sees cache rows 0 .. L_b - 1 (restricted by the window if W >= 1).
     Returns O: [B', Hq, d] and LSE: [B', Hq] in float64.  Only the valid
     prefix of each cache is read, so poisoned rows beyond it never matter.
-    ``rope_q = (cos_table, sin_table, rotary_dim)`` rotates the query at its
-    position L_b - 1; cached keys are taken as stored (a decode cache holds
+    ``rope_q = (cos_table, sin_table, rotary_dim[, store])`` rotates the
+    query at its position L_b - 1; cached keys are taken as stored (a decode cache holds
     keys already rotated at their own positions when they were appended).
     """
     B, Hq, d = q.shape

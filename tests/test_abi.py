@@ -72,6 +72,10 @@ int main(void) {
   F(fa_decode_params, block_table) F(fa_decode_params, page_size) F(fa_decode_params, pages_per_seq)
   F(fa_decode_params, num_pages) F(fa_decode_params, reserved1) F(fa_decode_params, kv_format)
   F(fa_decode_params, reserved2) F(fa_decode_params, k_scale) F(fa_decode_params, v_scale)
+  F(fa_decode_params, rope_cos) F(fa_decode_params, rope_sin) F(fa_decode_params, rotary_dim)
+  F(fa_decode_params, rope_max_pos) F(fa_prefill_params, rope_cos) F(fa_prefill_params, rope_sin)
+  F(fa_prefill_params, rotary_dim) F(fa_prefill_params, rope_max_pos)
+  F(fa_prefill_params, workspace) F(fa_prefill_params, workspace_bytes)
   return 0;
 }
 """
@@ -144,12 +148,39 @@ def _prefill(**kw):
     (dict(o=FAKE + 2), _lib.FA_ERR_UNSUPPORTED, "aligned"),
     (dict(k_stride=[1 << 30, 1 << 25, 128]), _lib.FA_ERR_UNSUPPORTED, "2^25"),
     (dict(v_stride=[1 << 30, 1 << 25, 128]), _lib.FA_ERR_UNSUPPORTED, "2^25"),
+    # RoPE
+    (dict(rotary_dim=4, rope_max_pos=100), _lib.FA_ERR_UNSUPPORTED, "rotary_dim"),
+    (dict(rotary_dim=136, rope_max_pos=100), _lib.FA_ERR_UNSUPPORTED, "rotary_dim"),
+    (dict(rotary_dim=-8, rope_max_pos=100), _lib.FA_ERR_UNSUPPORTED, "rotary_dim"),
+    (dict(rotary_dim=64, rope_max_pos=99), _lib.FA_ERR_INVALID_ARG, "rope_max_pos"),
+    (dict(rotary_dim=64, rope_max_pos=100, rope_cos=None, rope_sin=FAKE + 32768),
+     _lib.FA_ERR_INVALID_ARG, "rope_cos"),
+    (dict(rotary_dim=64, rope_max_pos=100, rope_cos=FAKE + 28680, rope_sin=FAKE + 32768),
+     _lib.FA_ERR_UNSUPPORTED, "16-byte"),
+    (dict(rotary_dim=64, rope_max_pos=100, rope_cos=FAKE + 28672, rope_sin=FAKE + 32768),
+     _lib.FA_ERR_WORKSPACE, "workspace is NULL"),
+    (dict(rotary_dim=64, rope_max_pos=100, rope_cos=FAKE + 28672, rope_sin=FAKE + 32768,
+          workspace=FAKE + 65536, workspace_bytes=2 * 100 * 2 * 128 * 2 - 1),
+     _lib.FA_ERR_WORKSPACE, "too small"),
+    (dict(rotary_dim=64, rope_max_pos=100, rope_cos=FAKE + 28672, rope_sin=FAKE + 32768,
+          workspace=FAKE + 65544, workspace_bytes=1 << 30), _lib.FA_ERR_WORKSPACE, "aligned"),
 ])
 def test_prefill_validation(lib, kw, status, needle):
     p = _prefill(**kw)
     st = _lib.prefill_fwd(p, 0)
     assert st == status, (_lib.status_str(st), _lib.last_error())
     assert needle in _lib.last_error()
+
+
+def test_prefill_workspace_size(lib):
+    # only bf16 with RoPE needs a workspace: the rotated copy of K
+    assert _lib.prefill_workspace_size(_prefill()) == (_lib.FA_OK, 0)
+    p = _prefill(rotary_dim=64, rope_max_pos=100)
+    assert _lib.prefill_workspace_size(p) == (_lib.FA_OK, 2 * 100 * 2 * 128 * 2)
+    p = _prefill(dtype=_lib.FA_DTYPE_F32, rotary_dim=64, rope_max_pos=100)
+    assert _lib.prefill_workspace_size(p) == (_lib.FA_OK, 0)
+    p = _prefill(rotary_dim=12, rope_max_pos=100)
+    assert _lib.prefill_workspace_size(p)[0] == _lib.FA_ERR_UNSUPPORTED
 
 
 def test_prefill_fp32_stride_rule(lib):
@@ -212,6 +243,10 @@ def _decode(**kw):
     (dict(kv_format=1, k_scale=None, v_scale=FAKE + 28800), _lib.FA_ERR_INVALID_ARG, "non-NULL"),
     (dict(kv_format=1, k_scale=FAKE + 28674, v_scale=FAKE + 28800), _lib.FA_ERR_INVALID_ARG,
      "4-byte aligned"),
+    (dict(rotary_dim=12, rope_max_pos=8192), _lib.FA_ERR_UNSUPPORTED, "rotary_dim"),
+    (dict(rotary_dim=64, rope_max_pos=8191), _lib.FA_ERR_INVALID_ARG, "rope_max_pos"),
+    (dict(rotary_dim=64, rope_max_pos=8192, rope_cos=FAKE + 28680, rope_sin=FAKE + 32768),
+     _lib.FA_ERR_UNSUPPORTED, "16-byte"),
     # paged-cache fields without a table, and bad paged parameters
     (dict(page_size=16), _lib.FA_ERR_INVALID_ARG, "without a block_table"),
     (dict(num_pages=4), _lib.FA_ERR_INVALID_ARG, "without a block_table"),
@@ -240,7 +275,7 @@ def test_decode_validation(lib, kw, status, needle):
     assert st == status, (_lib.status_str(st), _lib.last_error())
     assert needle in _lib.last_error()
     st2, _ = _lib.decode_workspace_size(p)
-    if needle in ("seqlens_k", "aligned", "4-byte", "non-NULL", "4-byte aligned"):
+    if needle in ("seqlens_k", "aligned", "4-byte", "non-NULL", "4-byte aligned", "16-byte"):
         # sizing the workspace needs shapes only, never the data pointers
         assert st2 == _lib.FA_OK
     else:

@@ -788,3 +788,18 @@ def test_rope_decode_query_at_last_position():
                                   causal=True, rope=rope)
         np.testing.assert_allclose(o[b], ro[0, 0], rtol=0, atol=1e-13)
         np.testing.assert_allclose(l[b], rl[0, :, 0], rtol=0, atol=1e-13)
+
+
+def test_round_to_dtype_single_rounding_to_nearest_even():
+    # ties go to the even neighbour; a value just above a tie goes up, which
+    # rounding through fp32 first (double rounding) would get wrong
+    vals = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -40,
+                     -(1.0 + 2.0 ** -8 + 2.0 ** -40), 0.0, 3.0])
+    want = np.array([1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -(1.0 + 2.0 ** -7), 0.0, 3.0])
+    assert np.array_equal(oracle.round_to_dtype(vals, "bf16"), want)
+    x = np.random.default_rng(3).standard_normal(50000).astype(np.float32) * 30
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.round_to_dtype(x.astype(np.float64), "bf16"), ref)
+    y = np.random.default_rng(4).standard_normal(1000)
+    assert np.array_equal(oracle.round_to_dtype(y, "f32"), y.astype(np.float32).astype(np.float64))
+    assert np.array_equal(oracle.round_to_dtype(y, None), y)

@@ -23,7 +23,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import FAError  # noqa: F401
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "FAError", "load_library"]
+__all__ = ["prefill", "prefill_workspace_size", "decode", "decode_workspace_size", "FAError",
+           "load_library"]
 
 
 def load_library():
@@ -80,9 +81,49 @@ def _slopes(x, H, device):
     return x
 
 
+def _rope(rope_cos, rope_sin, rotary_dim, device):
+    """(cos, sin, rotary_dim, max_pos) device tables, or None without RoPE."""
+    torch = _torch()
+    if rope_cos is None and rope_sin is None:
+        return None
+    if rope_cos is None or rope_sin is None:
+        raise ValueError("RoPE needs both rope_cos and rope_sin")
+    c = rope_cos.to(device=device, dtype=torch.float32).contiguous()
+    s = rope_sin.to(device=device, dtype=torch.float32).contiguous()
+    if c.dim() != 2 or c.shape != s.shape:
+        raise ValueError("rope_cos and rope_sin must both be [max_pos, rotary_dim / 2]")
+    rdim = 2 * c.shape[1] if rotary_dim is None else int(rotary_dim)
+    if rdim > 2 * c.shape[1]:
+        raise ValueError("rotary_dim exceeds the tables' width")
+    # the kernels index the tables with a row stride of rotary_dim / 2
+    if 2 * c.shape[1] != rdim:
+        c, s = c[:, :rdim // 2].contiguous(), s[:, :rdim // 2].contiguous()
+    return c, s, rdim, c.shape[0]
+
+
+def prefill_workspace_size(q, k, *, rope_cos=None, rope_sin=None, rotary_dim=None) -> int:
+    """Workspace bytes ``prefill`` needs (a rotated copy of K for bf16 with
+    RoPE, else 0); host-only."""
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if rope_cos is None:
+        return 0
+    rdim = 2 * rope_cos.shape[1] if rotary_dim is None else int(rotary_dim)
+    p = _lib.PrefillParams()
+    p.dtype = _dtype_code(q)
+    p.batch, p.seqlen_q, p.seqlen_k = B, Nq, Nk
+    p.heads_q, p.heads_kv, p.head_dim = Hq, Hkv, d
+    p.window_left, p.softmax_scale = -1, 1.0
+    p.rotary_dim, p.rope_max_pos = rdim, rope_cos.shape[0]
+    st, n = _lib.prefill_workspace_size(p)
+    _lib.check(st, "fa_prefill_workspace_size")
+    return n
+
+
 def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[float] = None,
             seqlens_q=None, seqlens_k=None, out=None, lse=None, return_lse: bool = True,
-            alibi_slopes=None) -> Tuple[object, object]:
+            alibi_slopes=None, rope_cos=None, rope_sin=None, rotary_dim=None,
+            workspace=None) -> Tuple[object, object]:
     """Fused attention forward for a batch of sequences.
 
     q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (any strides with a unit last
@@ -93,6 +134,11 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     valid lengths (rows past ``seqlens_q`` come back as O = 0, LSE = -inf).
     ``alibi_slopes`` (one value per query head) adds the ALiBi bias
     -slope_h * |pos_i - j| to the scaled scores, pos_i = i + Lk - Lq.
+    RoPE: ``rope_cos`` / ``rope_sin`` ([max_pos, rotary_dim / 2] tables;
+    ``rotary_dim`` defaults to twice their width) rotate adjacent pairs of the
+    first rotary_dim dims of q (at pos_i) and k (at j) before the products.
+    bf16 with RoPE needs a workspace (allocated here unless ``workspace``, a
+    uint8 GPU tensor of ``prefill_workspace_size`` bytes, is passed).
     """
     torch = _torch()
     _require_gpu(q, k, v)
@@ -115,6 +161,7 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     sq = _seqlens(seqlens_q, B, dev)
     sk = _seqlens(seqlens_k, B, dev)
     al = _slopes(alibi_slopes, Hq, dev)
+    rope = _rope(rope_cos, rope_sin, rotary_dim, dev)
     p = _lib.PrefillParams()
     p.dtype = _dtype_code(q)
     p.batch, p.seqlen_q, p.seqlen_k = B, Nq, Nk
@@ -131,6 +178,16 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     p.v_stride[:] = [v.stride(0), v.stride(1), v.stride(2)]
     p.o_stride[:] = [out.stride(0), out.stride(1), out.stride(2)]
     p.alibi_slopes = al.data_ptr() if al is not None else None
+    if rope is not None:
+        p.rope_cos, p.rope_sin = rope[0].data_ptr(), rope[1].data_ptr()
+        p.rotary_dim, p.rope_max_pos = rope[2], rope[3]
+        st, need = _lib.prefill_workspace_size(p)
+        _lib.check(st, "fa_prefill_workspace_size")
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            p.workspace = workspace.data_ptr()
+            p.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(_lib.prefill_fwd(p, _stream(dev)), "fa_prefill_fwd")
     return out, (lse if return_lse else None)
 
@@ -161,7 +218,7 @@ def _kv_scales(x, Hkv, device):
 
 
 def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys, al=None,
-                   table=None, capacity=None, scales=None):
+                   table=None, capacity=None, scales=None, rope=None):
     B, Hq, d = q.shape
     _, cap, Hkv, _ = k_cache.shape
     if table is not None:
@@ -193,6 +250,9 @@ def _decode_params(q, k_cache, v_cache, sk, out, lse, scale, window, chunk_keys,
     if scales is not None:
         p.kv_format = _lib.FA_KV_FP8_E4M3
         p.k_scale, p.v_scale = scales[0].data_ptr(), scales[1].data_ptr()
+    if rope is not None:
+        p.rope_cos, p.rope_sin = rope[0].data_ptr(), rope[1].data_ptr()
+        p.rotary_dim, p.rope_max_pos = rope[2], rope[3]
     return p
 
 
@@ -230,7 +290,7 @@ def decode_workspace_size(q, k_cache, v_cache, *, scale=None, window: int = -1,
 def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, window: int = -1,
            chunk_keys: int = 0, workspace=None, out=None, lse=None, return_lse: bool = True,
            alibi_slopes=None, block_table=None, capacity: Optional[int] = None,
-           k_scale=None, v_scale=None):
+           k_scale=None, v_scale=None, rope_cos=None, rope_sin=None, rotary_dim=None):
     """Single-token decode over a KV cache, contiguous or paged.
 
     q: [B, Hq, d]; k_cache, v_cache: [B, capacity, Hkv, d]; seqlens_k: [B]
@@ -249,6 +309,10 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     hold OCP FP8 E4M3 values; ``k_scale`` and ``v_scale`` (one fp32 value per
     KV head, or one float for all) give element = scale * E4M3(code).  q and
     the output stay bf16.
+
+    RoPE: ``rope_cos`` / ``rope_sin`` tables ([max_pos, rotary_dim / 2])
+    rotate the query at its position L_b - 1; cached keys are used as stored
+    (already rotated when they were appended).
     """
     torch = _torch()
     _require_gpu(q, k_cache, v_cache)
@@ -276,8 +340,9 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     if fp8:
         Hkv = k_cache.shape[2]
         scales = (_kv_scales(k_scale, Hkv, dev), _kv_scales(v_scale, Hkv, dev))
+    rope = _rope(rope_cos, rope_sin, rotary_dim, dev)
     p = _decode_params(q, k_cache, v_cache, sk, out, lse if return_lse else None, scale, window,
-                       chunk_keys, al, table, capacity, scales)
+                       chunk_keys, al, table, capacity, scales, rope)
     st, need = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     if workspace is None:

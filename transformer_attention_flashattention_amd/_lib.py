@@ -26,8 +26,8 @@ FA_KV_PLAIN = 0
 FA_KV_FP8_E4M3 = 1
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_prefill_fwd", "fa_decode_workspace_size", "fa_decode_fwd",
-           "fa_status_str", "fa_last_error_message", "fa_abi_version")
+EXPORTS = ("fa_prefill_fwd", "fa_prefill_workspace_size", "fa_decode_workspace_size",
+           "fa_decode_fwd", "fa_status_str", "fa_last_error_message", "fa_abi_version")
 
 _i64x3 = ctypes.c_int64 * 3
 _i64x2 = ctypes.c_int64 * 2
@@ -57,6 +57,12 @@ class PrefillParams(ctypes.Structure):
         ("v_stride", _i64x3),
         ("o_stride", _i64x3),
         ("alibi_slopes", ctypes.c_void_p),
+        ("rope_cos", ctypes.c_void_p),
+        ("rope_sin", ctypes.c_void_p),
+        ("rotary_dim", ctypes.c_int32),
+        ("rope_max_pos", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -92,6 +98,10 @@ class DecodeParams(ctypes.Structure):
         ("reserved2", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("rope_cos", ctypes.c_void_p),
+        ("rope_sin", ctypes.c_void_p),
+        ("rotary_dim", ctypes.c_int32),
+        ("rope_max_pos", ctypes.c_int32),
     ]
 
 
@@ -118,6 +128,9 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.fa_prefill_fwd.argtypes = [ctypes.POINTER(PrefillParams), ctypes.c_void_p]
     lib.fa_prefill_fwd.restype = ctypes.c_int
+    lib.fa_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams),
+                                              ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_prefill_workspace_size.restype = ctypes.c_int
     lib.fa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams),
                                              ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_decode_workspace_size.restype = ctypes.c_int
@@ -149,6 +162,12 @@ def check(status: int, func: str) -> None:
 
 def prefill_fwd(params: PrefillParams, stream: int) -> int:
     return load().fa_prefill_fwd(ctypes.byref(params), ctypes.c_void_p(stream))
+
+
+def prefill_workspace_size(params: PrefillParams) -> tuple:
+    n = ctypes.c_size_t(0)
+    st = load().fa_prefill_workspace_size(ctypes.byref(params), ctypes.byref(n))
+    return st, n.value
 
 
 def decode_workspace_size(params: DecodeParams) -> tuple:

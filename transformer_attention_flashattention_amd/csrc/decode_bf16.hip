@@ -256,6 +256,28 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         }
     }
 
+    // RoPE: the query sits at position L - 1 (L >= 1 for every work item);
+    // each u32 of qr is one adjacent pair of dims, turned by its angle and
+    // rounded back to bf16 (cached keys are stored already rotated)
+    if (a.rotary_dim > 0) {
+        const int rhalf = a.rotary_dim / 2;
+        const float *cr = a.rope_cos + (int64_t)(L - 1) * rhalf;
+        const float *sr = a.rope_sin + (int64_t)(L - 1) * rhalf;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int pr = KV8 ? 8 * s_sub + k : (k < 4 ? 4 * s_sub + k : D / 4 + 4 * s_sub + (k - 4));
+            if (pr < rhalf) {
+                const float c = cr[pr], sn = sr[pr];
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    const bf16x2 v = __builtin_bit_cast(bf16x2, qr[g][k]);
+                    const float x = (float)v[0], y = (float)v[1];
+                    qr[g][k] = pack_bf16x2(__builtin_fmaf(x, c, -y * sn), __builtin_fmaf(x, sn, y * c));
+                }
+            }
+        }
+    }
+
     // running state (m, the reference, is uniform across the wavefront)
     float m_ref[GT], o[GT][8];
     float l_part = 0.f;                                // this lane's share of the sum of head my_g

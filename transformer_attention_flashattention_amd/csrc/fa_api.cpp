@@ -53,6 +53,24 @@ fa_status check_strides(const char *name, const int64_t *st, int n, int vec) {
     return FA_OK;
 }
 
+// RoPE tables: rotary_dim a multiple of 8 up to head_dim (whole 16-byte
+// pieces of 4 pairs), tables 16-byte aligned and long enough for `positions`.
+fa_status check_rope(int rotary_dim, int max_pos, const float *c, const float *sn, int head_dim,
+                     int positions, bool need_pointers) {
+    if (rotary_dim == 0) return FA_OK;
+    if (rotary_dim < 0 || rotary_dim % 8 != 0 || rotary_dim > head_dim)
+        return fail(FA_ERR_UNSUPPORTED, "rotary_dim must be 0 or a multiple of 8 up to head_dim (got %d)",
+                    rotary_dim);
+    if (max_pos < positions)
+        return fail(FA_ERR_INVALID_ARG, "rope_max_pos (%d) must cover %d positions", max_pos, positions);
+    if (need_pointers) {
+        if (!c || !sn) return fail(FA_ERR_INVALID_ARG, "rope_cos and rope_sin must be non-NULL with RoPE");
+        if (!aligned16(c) || !aligned16(sn))
+            return fail(FA_ERR_UNSUPPORTED, "rope_cos and rope_sin must be 16-byte aligned");
+    }
+    return FA_OK;
+}
+
 #define FA_TRY(expr)                      \
     do {                                  \
         fa_status _s = (expr);            \
@@ -103,6 +121,8 @@ fa_status validate_decode(const fa_decode_params *p) {
         return fail(FA_ERR_INVALID_ARG, "unknown kv_format %d", p->kv_format);
     if (p->kv_format == FA_KV_PLAIN && (p->k_scale || p->v_scale))
         return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be NULL with FA_KV_PLAIN");
+    FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
+                      p->cache_capacity, false));
     if (p->block_table) {
         if (p->page_size < fa::kDecodePageUnit || p->page_size > 65536 ||
             p->page_size % fa::kDecodePageUnit != 0)
@@ -139,6 +159,8 @@ fa_status validate_decode_pointers(const fa_decode_params *p) {
         return fail(FA_ERR_INVALID_ARG, "o must be 2-byte aligned");
     if ((reinterpret_cast<uintptr_t>(p->block_table) & 3u) != 0)
         return fail(FA_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+    FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
+                      p->cache_capacity, true));
     if (p->kv_format == FA_KV_FP8_E4M3) {
         if (!p->k_scale || !p->v_scale)
             return fail(FA_ERR_INVALID_ARG, "k_scale and v_scale must be non-NULL with FA_KV_FP8_E4M3");
@@ -157,26 +179,13 @@ size_t decode_ws_bytes(const fa_decode_params *p, int chunk) {
     return o_bytes + ml_bytes;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
-
-const char *fa_status_str(fa_status s) {
-    switch (s) {
-        case FA_OK: return "FA_OK";
-        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
-        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
-        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
-        case FA_ERR_HIP: return "FA_ERR_HIP";
-    }
-    return "FA_ERR_UNKNOWN";
+// Workspace of a prefill call: the rotated copy of K (bf16 with RoPE only).
+size_t prefill_ws_bytes(const fa_prefill_params *p) {
+    if (p->rotary_dim == 0 || p->dtype != FA_DTYPE_BF16) return 0;
+    return (size_t)p->batch * p->seqlen_k * p->heads_kv * p->head_dim * 2;
 }
 
-const char *fa_last_error_message(void) { return g_last_error.c_str(); }
-
-fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
+fa_status validate_prefill(const fa_prefill_params *p) {
     if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
     if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32)
         return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
@@ -201,12 +210,55 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     // the bf16 kernel addresses the rows of one 64-key tile with 32-bit byte offsets
     if (p->dtype == FA_DTYPE_BF16 && (p->k_stride[1] >= (1LL << 25) || p->v_stride[1] >= (1LL << 25)))
         return fail(FA_ERR_UNSUPPORTED, "k_stride[1] and v_stride[1] must be below 2^25 elements for bf16");
+    FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
+                      p->seqlen_k, false));
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char *fa_status_str(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+const char *fa_last_error_message(void) { return g_last_error.c_str(); }
+
+fa_status fa_prefill_workspace_size(const fa_prefill_params *p, size_t *bytes) {
+    if (!bytes) return fail(FA_ERR_INVALID_ARG, "bytes is NULL");
+    FA_TRY(validate_prefill(p));
+    *bytes = prefill_ws_bytes(p);
+    return ok();
+}
+
+fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
+    FA_TRY(validate_prefill(p));
     if (p->batch == 0 || p->seqlen_q == 0) return ok();
     if (!p->q || !p->o) return fail(FA_ERR_INVALID_ARG, "q and o must be non-NULL");
     if (p->seqlen_k > 0 && (!p->k || !p->v))
         return fail(FA_ERR_INVALID_ARG, "k and v must be non-NULL when seqlen_k > 0");
     if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
         return fail(FA_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+    FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
+                      p->seqlen_k, true));
+    const size_t ws_need = prefill_ws_bytes(p);
+    if (ws_need > 0 && p->seqlen_k > 0) {
+        if (!p->workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", ws_need);
+        if (!aligned16(p->workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        if (p->workspace_bytes < 0 || (size_t)p->workspace_bytes < ws_need)
+            return fail(FA_ERR_WORKSPACE, "workspace too small: %lld < %zu bytes",
+                        (long long)p->workspace_bytes, ws_need);
+    }
 
     fa::PrefillArgs a{};
     a.q = p->q; a.k = p->k; a.v = p->v; a.o = p->o; a.lse = p->lse;
@@ -221,12 +273,29 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     a.scale = p->softmax_scale;
     a.scale_log2 = p->softmax_scale * kLog2e;
     a.alibi = p->alibi_slopes;
+    if (p->rotary_dim > 0) {
+        a.rope_cos = p->rope_cos; a.rope_sin = p->rope_sin; a.rotary_dim = p->rotary_dim;
+    }
     const int bm = p->dtype == FA_DTYPE_BF16 ? fa::kPrefillBM : fa::kPrefillF32BM;
     a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
     if ((int64_t)a.num_q_tiles * a.heads_q * a.batch > 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (ws_need > 0 && p->seqlen_k > 0) {
+        // bf16 with RoPE: rotate K once into the workspace, then attend to it
+        fa::RopeKArgs r{};
+        r.k = p->k; r.out = p->workspace; r.seqlens_k = p->seqlens_k;
+        r.k_sb = p->k_stride[0]; r.k_ss = p->k_stride[1]; r.k_sh = p->k_stride[2];
+        r.batch = p->batch; r.seqlen_k = p->seqlen_k; r.heads_kv = p->heads_kv;
+        r.rope_cos = p->rope_cos; r.rope_sin = p->rope_sin; r.rotary_dim = p->rotary_dim;
+        const hipError_t er = fa::launch_rope_k_bf16(r, p->head_dim, s);
+        if (er != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(er));
+        a.k = p->workspace;
+        a.k_sb = (int64_t)p->seqlen_k * p->heads_kv * p->head_dim;
+        a.k_ss = (int64_t)p->heads_kv * p->head_dim;
+        a.k_sh = p->head_dim;
+    }
     const hipError_t e = p->dtype == FA_DTYPE_BF16 ? fa::launch_prefill_bf16(a, p->head_dim, s)
                                                    : fa::launch_prefill_f32(a, p->head_dim, s);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -283,6 +352,9 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     a.page_size = p->page_size; a.pages_per_seq = p->pages_per_seq; a.num_pages = p->num_pages;
     a.kv_fp8 = p->kv_format == FA_KV_FP8_E4M3;
     a.k_scale = p->k_scale; a.v_scale = p->v_scale;
+    if (p->rotary_dim > 0) {
+        a.rope_cos = p->rope_cos; a.rope_sin = p->rope_sin; a.rotary_dim = p->rotary_dim;
+    }
     const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
     const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
     a.ws_o = static_cast<float *>(workspace);

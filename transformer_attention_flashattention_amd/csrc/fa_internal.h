@@ -25,6 +25,20 @@ struct PrefillArgs {
     float scale;                   // softmax_scale
     int32_t num_q_tiles;
     const float *alibi;            // ALiBi slopes [heads_q] or null
+    const float *rope_cos, *rope_sin;  // RoPE tables [max_pos, rotary_dim / 2], or null
+    int32_t rotary_dim;            // 0 = no RoPE
+};
+
+// K rotation pass (bf16 prefill with RoPE): rows j < Lk of every KV head,
+// rotated at position j, into a contiguous [batch, seqlen_k, heads_kv, D] copy.
+struct RopeKArgs {
+    const void *k;
+    void *out;
+    const int32_t *seqlens_k;
+    int64_t k_sb, k_ss, k_sh;
+    int32_t batch, seqlen_k, heads_kv;
+    const float *rope_cos, *rope_sin;
+    int32_t rotary_dim;
 };
 
 struct DecodeArgs {
@@ -50,11 +64,14 @@ struct DecodeArgs {
     int32_t kv_fp8;                // 1: K/V are FP8 E4M3 codes scaled by k_scale / v_scale
     const float *k_scale, *v_scale;  // [heads_kv] (FP8 cache)
     int32_t origin_align;          // chunk grid origin alignment (set by the launcher)
+    const float *rope_cos, *rope_sin;  // RoPE tables for the query at L - 1, or null
+    int32_t rotary_dim;            // 0 = no RoPE
 };
 
 // Each launcher enqueues its kernel(s) and returns the launch status.
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_wg,
                               hipStream_t s);
 

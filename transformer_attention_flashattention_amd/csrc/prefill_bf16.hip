@@ -171,8 +171,9 @@ __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
                  : "memory", "m0");
 }
 
-// D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores.
-template <int D, bool ALIBI>
+// D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores;
+// ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated).
+template <int D, bool ALIBI, bool ROPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
@@ -248,6 +249,31 @@ void prefill_bf16_kernel(PrefillArgs a) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (ok) v = *(const u32x4 *)(row + ks * 16);
             qf[ks] = __builtin_bit_cast(bf16x8, v);
+        }
+        // RoPE: the lane's 8 dims of a k-step are 4 adjacent pairs, turned by
+        // the angles of its row's position (qi + Lk - Lq); the result is
+        // rounded to bf16, the operand precision
+        if constexpr (ROPE) {
+            if (ok) {
+                const int rhalf = a.rotary_dim / 2;
+                const float *cr = a.rope_cos + (int64_t)(qi + offset) * rhalf;
+                const float *sr = a.rope_sin + (int64_t)(qi + offset) * rhalf;
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const int p0 = ks * 8 + half * 4;           // first pair of the 8 dims
+                    if (2 * p0 < a.rotary_dim) {                 // rotary_dim: whole groups of 4 pairs
+                        const float4 c = *(const float4 *)(cr + p0);
+                        const float4 sn = *(const float4 *)(sr + p0);
+                        const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = (float)qf[ks][2 * e], y = (float)qf[ks][2 * e + 1];
+                            qf[ks][2 * e] = (__bf16)__builtin_fmaf(x, cc[e], -y * ss[e]);
+                            qf[ks][2 * e + 1] = (__bf16)__builtin_fmaf(x, ss[e], y * cc[e]);
+                        }
+                    }
+                }
+            }
         }
     }
 
@@ -533,12 +559,23 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s
     const dim3 grid((unsigned)a.num_q_tiles * a.heads_q * a.batch);
     const dim3 block(NTHREADS);
     const bool alibi = a.alibi != nullptr;
+    const bool rope = a.rotary_dim > 0;
     if (head_dim == 128) {
-        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+        if (rope) {
+            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, true>), grid, block, 0, s, a);
+        } else {
+            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false>), grid, block, 0, s, a);
+        }
     } else {
-        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+        if (rope) {
+            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, true, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<64, false, true>), grid, block, 0, s, a);
+        } else {
+            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, true, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<64, false, false>), grid, block, 0, s, a);
+        }
     }
     return hipGetLastError();
 }

@@ -57,11 +57,31 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
     const float *Kp = (const float *)a.k + b * a.k_sb + kvh * a.k_sh;
     const float *Vp = (const float *)a.v + b * a.v_sb + kvh * a.v_sh;
 
-    // stage this workgroup's query rows (zero outside the valid length)
-    for (int idx = tid; idx < BM * D; idx += BM) {
-        const int r = idx / D, d = idx - (idx / D) * D;
+    // RoPE: pair (2p, 2p + 1) at position m turns by the table's angle
+    // (x, y) -> (x c - y s, x s + y c); queries sit at i + Lk - Lq, keys at j
+    const int rhalf = a.rotary_dim / 2;
+    auto rotate = [&](float &x, float &y, int m, int p) {
+        if (p < rhalf) {
+            const float c = a.rope_cos[(int64_t)m * rhalf + p], sn = a.rope_sin[(int64_t)m * rhalf + p];
+            const float x0 = x;
+            x = __builtin_fmaf(x0, c, -y * sn);
+            y = __builtin_fmaf(x0, sn, y * c);
+        }
+    };
+
+    // stage this workgroup's query rows (zero outside the valid length), a
+    // pair of dims per step
+    for (int idx = tid; idx < BM * (D / 2); idx += BM) {
+        const int r = idx / (D / 2), p = idx - (idx / (D / 2)) * (D / 2);
         const int i = q0 + r;
-        Qs[r][d] = (i < Lq) ? Qp[(int64_t)i * a.q_ss + d] : 0.f;
+        float x = 0.f, y = 0.f;
+        if (i < Lq) {
+            x = Qp[(int64_t)i * a.q_ss + 2 * p];
+            y = Qp[(int64_t)i * a.q_ss + 2 * p + 1];
+            rotate(x, y, i + offset, p);
+        }
+        Qs[r][2 * p] = x;
+        Qs[r][2 * p + 1] = y;
     }
 
     const int qi = q0 + tid;
@@ -77,10 +97,21 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
     for (int t = t_begin; t < t_end; ++t) {
         const int k0 = t * BN;
         __syncthreads();
+        for (int idx = tid; idx < BN * (D / 2); idx += BM) {
+            const int r = idx / (D / 2), p = idx - (idx / (D / 2)) * (D / 2);
+            const int j = k0 + r;
+            float x = 0.f, y = 0.f;
+            if (j < Lk) {
+                x = Kp[(int64_t)j * a.k_ss + 2 * p];
+                y = Kp[(int64_t)j * a.k_ss + 2 * p + 1];
+                rotate(x, y, j, p);
+            }
+            Ks[r][2 * p] = x;
+            Ks[r][2 * p + 1] = y;
+        }
         for (int idx = tid; idx < BN * D; idx += BM) {
             const int r = idx / D, d = idx - (idx / D) * D;
             const int j = k0 + r;
-            Ks[r][d] = (j < Lk) ? Kp[(int64_t)j * a.k_ss + d] : 0.f;
             Vs[r][d] = (j < Lk) ? Vp[(int64_t)j * a.v_ss + d] : 0.f;
         }
         __syncthreads();
