@@ -14,8 +14,9 @@ library), so the per-call averages are kernel time plus launch gaps.
 After the timed steps, the same two calls are timed with ALiBi slopes
 (reported under "alibi"), and the decode call over the same logical cache
 held in a paged pool of 16-row pages in shuffled order (under "paged") and
-as FP8 E4M3 codes with per-KV-head scales (under "fp8_kv"); none of these is
-part of the step.
+as FP8 E4M3 codes with per-KV-head scales (under "fp8_kv"), and the prefill
+with RoPE over all 128 dims (under "rope"); none of these is part of the
+step.
 
 Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
 algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
@@ -217,6 +218,28 @@ def main():
     pre_a = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_a]))
     dec_a = float(np.mean([e[1].elapsed_time(e[2]) for e in ev_a]))
 
+    # the prefill with RoPE (tables for base 10000 over all 128 dims): the
+    # bf16 K rotation pass plus the attention kernel rotating Q at load
+    half = d // 2
+    inv = 10000.0 ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
+    ang = np.arange(N, dtype=np.float64)[:, None] * inv[None, :]
+    rc = torch.from_numpy(np.cos(ang).astype(np.float32)).to(dev)
+    rs = torch.from_numpy(np.sin(ang).astype(np.float32)).to(dev)
+    wsr = torch.empty(fa.prefill_workspace_size(q, k, rope_cos=rc, rope_sin=rs), dtype=torch.uint8,
+                      device=dev)
+    fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse, rope_cos=rc, rope_sin=rs,
+               workspace=wsr)
+    torch.cuda.synchronize()
+    ev_r = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_alibi)]
+    for e in ev_r:
+        e[0].record()
+        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse, rope_cos=rc, rope_sin=rs,
+                   workspace=wsr)
+        e[1].record()
+    torch.cuda.synchronize()
+    pre_r = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_r]))
+    del wsr, rc, rs
+
     # the decode over a paged pool holding the same logical cache
     page = 16
     pp = workloads.make_workload_paged(5, page)
@@ -304,6 +327,9 @@ def main():
                   "decode_ms_mean": round(dec_a, 4),
                   "decode_gbs": round(dbytes / (dec_a * 1e-3) / 1e9, 1),
                   "calls": n_alibi},
+        "rope": {"rotary_dim": d, "prefill_ms_mean": round(pre_r, 4),
+                 "prefill_tflops": round(flops / (pre_r * 1e-3) / 1e12, 2),
+                 "note": "K rotation pass + attention with Q rotated at load", "calls": n_alibi},
         "fp8_kv": {"format": "e4m3", "decode_ms_mean": round(dec_f, 4),
                    "decode_gbs": round(fp8_bytes / (dec_f * 1e-3) / 1e9, 1),
                    "frac_of_hbm_peak": round(fp8_bytes / (dec_f * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -181,6 +181,9 @@ def test_prefill_workspace_size(lib):
     assert _lib.prefill_workspace_size(p) == (_lib.FA_OK, 0)
     p = _prefill(rotary_dim=12, rope_max_pos=100)
     assert _lib.prefill_workspace_size(p)[0] == _lib.FA_ERR_UNSUPPORTED
+    p = _prefill(batch=70000, rotary_dim=64, rope_max_pos=100)
+    assert _lib.prefill_workspace_size(p)[0] == _lib.FA_ERR_UNSUPPORTED
+    assert "65535" in _lib.last_error()
 
 
 def test_prefill_fp32_stride_rule(lib):

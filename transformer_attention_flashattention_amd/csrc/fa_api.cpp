@@ -212,6 +212,9 @@ fa_status validate_prefill(const fa_prefill_params *p) {
         return fail(FA_ERR_UNSUPPORTED, "k_stride[1] and v_stride[1] must be below 2^25 elements for bf16");
     FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
                       p->seqlen_k, false));
+    // the K rotation pass puts batch and KV head on the second and third grid axes
+    if (p->rotary_dim > 0 && p->dtype == FA_DTYPE_BF16 && (p->batch > 65535 || p->heads_kv > 65535))
+        return fail(FA_ERR_UNSUPPORTED, "RoPE with bf16 supports batch and heads_kv up to 65535");
     return FA_OK;
 }
 

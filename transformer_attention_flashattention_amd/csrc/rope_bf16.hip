@@ -11,7 +11,8 @@
 // row once (key j at position j) into a contiguous copy that the attention
 // kernel then reads; queries are rotated inside the attention kernel as they
 // are loaded.  The pass streams K once: one thread per 16-byte piece (8 dims,
-// 4 pairs) of a row, a grid-stride loop over [batch, key, KV head, piece].
+// 4 pairs) of a row; a workgroup covers 256 / (D / 8) consecutive keys of one
+// (batch, KV head), so no index needs a division.
 // Rows at or beyond a sequence's valid key length are neither read nor
 // written (the attention kernel never reads them either).
 #include "fa_internal.h"
@@ -33,42 +34,37 @@ __device__ __forceinline__ unsigned rotate_pair(unsigned xy, float c, float s) {
 
 template <int D>
 __global__ __launch_bounds__(256) void rope_k_bf16_kernel(RopeKArgs a) {
-    constexpr int PIECES = D / 8;
-    const int half = a.rotary_dim / 2;
-    const int64_t total = (int64_t)a.batch * a.seqlen_k * a.heads_kv * PIECES;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int piece = (int)(idx % PIECES);
-        int64_t row = idx / PIECES;                      // (b, j, kvh) in BSHD order
-        const int kvh = (int)(row % a.heads_kv);
-        row /= a.heads_kv;
-        const int j = (int)(row % a.seqlen_k);
-        const int b = (int)(row / a.seqlen_k);
-        const int Lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.seqlen_k) : a.seqlen_k;
-        if (j >= Lk) continue;
-        const unsigned short *src = (const unsigned short *)a.k + b * a.k_sb + (int64_t)j * a.k_ss +
-                                    kvh * a.k_sh + piece * 8;
-        u32x4 v = *(const u32x4 *)src;
-        if (piece * 8 < a.rotary_dim) {                  // rotary_dim is a multiple of 8
-            const float4 c = *(const float4 *)(a.rope_cos + (int64_t)j * half + piece * 4);
-            const float4 s = *(const float4 *)(a.rope_sin + (int64_t)j * half + piece * 4);
-            v[0] = rotate_pair(v[0], c.x, s.x);
-            v[1] = rotate_pair(v[1], c.y, s.y);
-            v[2] = rotate_pair(v[2], c.z, s.z);
-            v[3] = rotate_pair(v[3], c.w, s.w);
-        }
-        *(u32x4 *)((unsigned short *)a.out + idx * 8) = v;
+    constexpr int PIECES = D / 8;                        // 16-byte pieces per row
+    constexpr int KEYS = 256 / PIECES;                   // key rows per workgroup
+    const int piece = threadIdx.x % PIECES;
+    const int j = blockIdx.x * KEYS + threadIdx.x / PIECES;
+    const int b = blockIdx.y, kvh = blockIdx.z;
+    const int Lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.seqlen_k) : a.seqlen_k;
+    if (j >= Lk) return;
+    const unsigned short *src =
+        (const unsigned short *)a.k + b * a.k_sb + (int64_t)j * a.k_ss + kvh * a.k_sh + piece * 8;
+    u32x4 v = *(const u32x4 *)src;
+    if (piece * 8 < a.rotary_dim) {                      // rotary_dim is a multiple of 8
+        const int half = a.rotary_dim / 2;
+        const float4 c = *(const float4 *)(a.rope_cos + (int64_t)j * half + piece * 4);
+        const float4 s = *(const float4 *)(a.rope_sin + (int64_t)j * half + piece * 4);
+        v[0] = rotate_pair(v[0], c.x, s.x);
+        v[1] = rotate_pair(v[1], c.y, s.y);
+        v[2] = rotate_pair(v[2], c.z, s.z);
+        v[3] = rotate_pair(v[3], c.w, s.w);
     }
+    unsigned short *dst = (unsigned short *)a.out +
+                          (((int64_t)b * a.seqlen_k + j) * a.heads_kv + kvh) * D + piece * 8;
+    *(u32x4 *)dst = v;
 }
 
 }  // namespace
 
 hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, hipStream_t s) {
-    const int64_t pieces = (int64_t)a.batch * a.seqlen_k * a.heads_kv * (head_dim / 8);
-    const int64_t want = (pieces + 255) / 256;
-    const unsigned blocks = (unsigned)(want < 16384 ? (want > 0 ? want : 1) : 16384);
-    if (head_dim == 128) hipLaunchKernelGGL(rope_k_bf16_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(rope_k_bf16_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+    const int keys = 256 / (head_dim / 8);
+    const dim3 grid((unsigned)((a.seqlen_k + keys - 1) / keys), (unsigned)a.batch, (unsigned)a.heads_kv);
+    if (head_dim == 128) hipLaunchKernelGGL(rope_k_bf16_kernel<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(rope_k_bf16_kernel<64>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
