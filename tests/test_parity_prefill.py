@@ -302,14 +302,17 @@ def test_alibi_head_dim_64_and_fp32():
 
 def test_alibi_large_slopes_and_zero_slopes():
     """Huge slopes concentrate every row on its own key position (O -> V_pos);
-    zero slopes give bit-identical results to no ALiBi at all."""
+    zero slopes give the plain result (to rounding only: the ALiBi kernel
+    visits the key tiles last to first, so its sums run in another order)."""
     p = workloads.make_prefill(64, 1, 260, 260, 2, 2, 128, "bf16", causal=True)
     _alibi_case(p, [50.0, 200.0], "ALiBi huge slopes")
+    _alibi_case(p, [0.0, 0.0], "ALiBi zero slopes")
     q, k, v, sq, sk = prefill_inputs(p)
     o0, l0 = fa.prefill(q, k, v, causal=True, scale=p.scale)
     o1, l1 = fa.prefill(q, k, v, causal=True, scale=p.scale, alibi_slopes=[0.0, 0.0])
     torch.cuda.synchronize()
-    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert (o0.float() - o1.float()).abs().max().item() <= 2e-2
+    assert (l0 - l1).abs().max().item() <= 1e-5
 
 
 def test_alibi_causal_8k_sampled():

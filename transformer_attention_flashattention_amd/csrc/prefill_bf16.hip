@@ -234,6 +234,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
     }
 
+    // Order of the key tiles.  With ALiBi the bias grows toward a row's
+    // diagonal, so in key order every tile would raise the row max past the
+    // running reference and send the softmax step down its slow exact-max
+    // path; visiting the tiles from the last to the first puts the largest
+    // scores first.  Step j of the pipeline handles tile tile_of(j); the
+    // wavefront's range [w_lo, w_hi) is turned into step numbers to match.
+    auto tile_of = [&](int j) { return ALIBI ? ntiles - 1 - j : j; };
+    if constexpr (ALIBI) {
+        const int lo_ = w_lo;
+        w_lo = ntiles - w_hi;
+        w_hi = ntiles - lo_;
+    }
+
     const unsigned short *Qp = (const unsigned short *)a.q + b * a.q_sb + h * a.q_sh;
     const char *Kp = (const char *)((const unsigned short *)a.k + b * a.k_sb + kvh * a.k_sh);
     const char *Vp = (const char *)((const unsigned short *)a.v + b * a.v_sb + kvh * a.v_sh);
@@ -293,7 +306,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
     auto issue = [&](const char *base, int64_t row_bytes, const unsigned *loff, int t, char *buf,
                      bool is_k) {
-        const int k0 = (t_begin + t) * BN;
+        const int k0 = (t_begin + tile_of(t)) * BN;
         const char *tb = base + (int64_t)k0 * row_bytes;
         if (k0 + BN <= Lk) {
 #pragma unroll
@@ -421,7 +434,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // softmax step of tile j: mask, running max, P in bf16, row sums
     auto softmax_step = [&](int j) {
         if (!(j >= w_lo && j < w_hi)) return;
-        const int k0 = (t_begin + j) * BN;
+        const int k0 = (t_begin + tile_of(j)) * BN;
         const bool need_mask = (k0 + BN > Lk) ||
                                (a.causal && k0 + BN - 1 > q0w + offset) ||
                                (W > 0 && k0 <= q0w + 31 + offset - W);
