@@ -67,6 +67,12 @@ notes):
   largest finite value 448), with one fp32 scale per KV head for K and one
   for V; the element's value is ``scale * E4M3(code)``.  Attention over the
   dequantized cache is the decode above, unchanged;
+* explicit mask (the BERT page: the baseline adds ``mask`` to the scaled
+  scores, ``score = score + mask``, chapter 一; its fused replacement passes
+  the same tensor as ``attn_mask``, chapter 三; the benchmark builds it as
+  [b, 1, 1, n], chapter 五): an additive tensor, broadcast over batch,
+  heads and query rows as its shape allows, added to the scaled scores
+  before the implicit masks; -inf entries remove a key;
 * RoPE (the jsqmd.com page, section 三, rotary position encoding and its
   fusion into attention): the vector at position m is rotated pair by pair,
   each pair of adjacent dimensions (2p, 2p + 1) by its own angle; the page
@@ -192,7 +198,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
               rows: Optional[Sequence[int]] = None,
               heads: Optional[Sequence[int]] = None,
               alibi_slopes: Optional[Sequence[float]] = None,
-              rope: Optional[tuple] = None):
+              rope: Optional[tuple] = None,
+              attn_mask: Optional[np.ndarray] = None):
     """Reference attention forward.
 
     q: [B, Nq, Hq, d], k and v: [B, Nk, Hkv, d] (any real dtype; used as
@@ -206,6 +213,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     (at ``i + Lk - Lq``) and K rows (at ``j``) before the scores, rounding
     the rotated elements to ``store`` ("bf16", "f32" or None); only rows
     inside the valid lengths are rotated (the others are never visible).
+    ``attn_mask`` (float array broadcastable to [B, Hq, Nq, Nk]) is added to
+    the scaled scores.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -224,6 +233,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
         slopes = np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
         if slopes.shape != (Hq,):
             raise ValueError("alibi_slopes needs one value per query head")
+    if attn_mask is not None:
+        attn_mask = np.broadcast_to(np.asarray(attn_mask, dtype=np.float64), (B, Hq, Nq, Nk))
     o = np.zeros((B, len(rows), len(heads), d), dtype=np.float64)
     lse = np.zeros((B, len(heads), len(rows)), dtype=np.float64)
     for b in range(B):
@@ -238,6 +249,9 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
         for hi, h in enumerate(heads):
             kvh = h // group
             bias = None if alibi_slopes is None else alibi_bias(rows, Nk, Lq, Lk, slopes[h])
+            if attn_mask is not None:
+                extra = attn_mask[b, h][rows]
+                bias = extra if bias is None else bias + extra
             qb, kb = q[b, rows, h, :], k[b, :, kvh, :]
             if rope is not None:
                 qb, kb = qb.copy(), kb.copy()

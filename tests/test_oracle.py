@@ -803,3 +803,52 @@ def test_round_to_dtype_single_rounding_to_nearest_even():
     y = np.random.default_rng(4).standard_normal(1000)
     assert np.array_equal(oracle.round_to_dtype(y, "f32"), y.astype(np.float32).astype(np.float64))
     assert np.array_equal(oracle.round_to_dtype(y, None), y)
+
+
+# ---------------------------------------------------------------------------
+# Explicit additive mask
+# ---------------------------------------------------------------------------
+def test_mask_zero_and_padding_equivalences():
+    """A zero mask changes nothing; a key-padding mask of -inf (shape
+    [B, 1, 1, Nk], the BERT page's layout) equals valid key lengths."""
+    p = workloads.make_prefill(82, 3, 40, 40, 4, 2, 16, "f32")
+    q, k, v = _f64(p)
+    o0, l0 = oracle.attention(q, k, v, scale=0.3)
+    o1, l1 = oracle.attention(q, k, v, scale=0.3, attn_mask=np.zeros((3, 1, 1, 40)))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    lengths = [40, 13, 1]
+    pad = np.zeros((3, 1, 1, 40))
+    for b, L in enumerate(lengths):
+        pad[b, 0, 0, L:] = -np.inf
+    o2, l2 = oracle.attention(q, k, v, scale=0.3, attn_mask=pad)
+    o3, l3 = oracle.attention(q, k, v, scale=0.3, seqlens_k=lengths)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+
+
+def test_mask_as_bias_equals_alibi():
+    """A mask holding -m |pos_i - j| gives the ALiBi result (powers of two keep
+    both sides exact)."""
+    p = workloads.make_prefill(83, 1, 24, 30, 2, 1, 16, "f32", causal=True)
+    q, k, v = _f64(p)
+    slopes = np.array([0.5, 0.125], np.float32)
+    pos = np.arange(24)[:, None] + (30 - 24)
+    dist = np.abs(pos - np.arange(30)[None, :]).astype(np.float64)
+    mask = -slopes.astype(np.float64)[None, :, None, None] * dist[None, None]
+    o1, l1 = oracle.attention(q, k, v, scale=0.25, causal=True, alibi_slopes=slopes)
+    o2, l2 = oracle.attention(q, k, v, scale=0.25, causal=True, attn_mask=mask)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_mask_matches_torch_sdpa_float_mask():
+    p = workloads.make_prefill(84, 2, 20, 27, 3, 3, 8, "f32")
+    q, k, v = _f64(p)
+    mask = np.random.default_rng(5).standard_normal((2, 3, 20, 27)) * 3.0
+    mask[0, 1, 4, :20] = -np.inf
+    o, lse = oracle.attention(q, k, v, scale=0.35, attn_mask=mask)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(0, 2, 1, 3), torch.from_numpy(k).permute(0, 2, 1, 3),
+        torch.from_numpy(v).permute(0, 2, 1, 3), attn_mask=torch.from_numpy(mask),
+        scale=float(np.float32(0.35)))            # the scale is an fp32 argument
+    np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+    s = float(np.float32(0.35)) * np.einsum("bqhd,bkhd->bhqk", q, k) + mask
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-12)
