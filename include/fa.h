@@ -120,6 +120,20 @@ typedef enum {
  * scratch after the call) of at least fa_prefill_workspace_size() bytes.
  * With rotary_dim = 0 the tables and the workspace are ignored.
  *
+ * Explicit mask (the BERT page: score = score + mask before softmax in its
+ * baseline, chapter 一; passed as attn_mask to the fused operator, chapter
+ * 三): attn_mask, when not NULL, is an additive tensor in the call's dtype,
+ * read at element b * mask_stride[0] + h * mask_stride[1] + i *
+ * mask_stride[2] + j for query head h, row i < seqlen_q and key j <
+ * seqlen_k.  A stride of 0 broadcasts that dimension (the page's [b, 1, 1, n]
+ * key-padding mask is strides {n, 0, 0, 1}); mask_stride[3] must be 1.  The
+ * value is added to softmax_scale * q_i . k_j (after ALiBi, before the
+ * implicit masks); -inf removes the key.  Pointer 16-byte aligned;
+ * mask_stride[0..2] multiples of 8 elements (bf16) or 4 (fp32).  Values
+ * are read on the device and not validated.  The implicit masks stay the
+ * cheap way to express causal, window and padding: an explicit mask adds
+ * its bytes to every query tile's traffic.
+ *
  * Requirements: head_dim in {64, 128}; heads_q % heads_kv == 0;
  * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
  * window_left == -1 or >= 1; extents >= 0; seqlens arrays (if given) are
@@ -158,6 +172,8 @@ typedef struct {
     int32_t rope_max_pos;                /* rows of the tables (>= seqlen_k)     */
     void *workspace;                     /* bf16 RoPE only: rotated K            */
     int64_t workspace_bytes;
+    const void *attn_mask;               /* device additive mask (dtype) or NULL */
+    int64_t mask_stride[4];              /* elements: batch, head, row, key (=1) */
 } fa_prefill_params;
 
 /*
@@ -295,7 +311,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10400
+#define FA_ABI_VERSION 10500
 
 #ifdef __cplusplus
 }

@@ -76,6 +76,7 @@ int main(void) {
   F(fa_decode_params, rope_max_pos) F(fa_prefill_params, rope_cos) F(fa_prefill_params, rope_sin)
   F(fa_prefill_params, rotary_dim) F(fa_prefill_params, rope_max_pos)
   F(fa_prefill_params, workspace) F(fa_prefill_params, workspace_bytes)
+  F(fa_prefill_params, attn_mask) F(fa_prefill_params, mask_stride)
   return 0;
 }
 """
@@ -164,6 +165,15 @@ def _prefill(**kw):
      _lib.FA_ERR_WORKSPACE, "too small"),
     (dict(rotary_dim=64, rope_max_pos=100, rope_cos=FAKE + 28672, rope_sin=FAKE + 32768,
           workspace=FAKE + 65544, workspace_bytes=1 << 30), _lib.FA_ERR_WORKSPACE, "aligned"),
+    # explicit mask
+    (dict(attn_mask=FAKE + 40960, mask_stride=[100, 0, 0, 0]), _lib.FA_ERR_UNSUPPORTED,
+     "mask_stride[3]"),
+    (dict(attn_mask=FAKE + 40960, mask_stride=[100, 0, 0, 1]), _lib.FA_ERR_UNSUPPORTED,
+     "mask_stride[0]"),
+    (dict(attn_mask=FAKE + 40960, mask_stride=[104, 0, -8, 1]), _lib.FA_ERR_INVALID_ARG,
+     "mask_stride[2]"),
+    (dict(attn_mask=FAKE + 40962, mask_stride=[104, 0, 0, 1]), _lib.FA_ERR_UNSUPPORTED,
+     "attn_mask must be 16-byte aligned"),
 ])
 def test_prefill_validation(lib, kw, status, needle):
     p = _prefill(**kw)

@@ -101,6 +101,28 @@ def _rope(rope_cos, rope_sin, rotary_dim, device):
     return c, s, rdim, c.shape[0]
 
 
+def _mask(m, dtype, shape, device):
+    """The mask as a [B, Hq, Nq, Nk] view in q's dtype: broadcast dims keep
+    stride 0, keys are contiguous, and the other strides are whole 16-byte
+    vectors (rows are padded in a copy when they are not)."""
+    torch = _torch()
+    if m is None:
+        return None
+    m = m.to(device=device, dtype=dtype)
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    m = m.expand(*shape)
+    vec = 16 // m.element_size()
+    if m.stride(3) != 1 or any(st % vec for st in m.stride()[:3]) or m.data_ptr() % 16:
+        Nk = shape[3]
+        pad = (Nk + vec - 1) // vec * vec
+        keep = [sz if st != 0 else 1 for sz, st in zip(shape[:3], m.stride()[:3])]
+        buf = torch.empty(*keep, pad, dtype=dtype, device=device)
+        buf[..., :Nk] = m[tuple(slice(0, k) for k in keep)]
+        m = buf[..., :Nk].expand(*shape)
+    return m
+
+
 def prefill_workspace_size(q, k, *, rope_cos=None, rope_sin=None, rotary_dim=None) -> int:
     """Workspace bytes ``prefill`` needs (a rotated copy of K for bf16 with
     RoPE, else 0); host-only."""
@@ -123,7 +145,7 @@ def prefill_workspace_size(q, k, *, rope_cos=None, rope_sin=None, rotary_dim=Non
 def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[float] = None,
             seqlens_q=None, seqlens_k=None, out=None, lse=None, return_lse: bool = True,
             alibi_slopes=None, rope_cos=None, rope_sin=None, rotary_dim=None,
-            workspace=None) -> Tuple[object, object]:
+            workspace=None, attn_mask=None) -> Tuple[object, object]:
     """Fused attention forward for a batch of sequences.
 
     q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (any strides with a unit last
@@ -139,6 +161,10 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     first rotary_dim dims of q (at pos_i) and k (at j) before the products.
     bf16 with RoPE needs a workspace (allocated here unless ``workspace``, a
     uint8 GPU tensor of ``prefill_workspace_size`` bytes, is passed).
+    ``attn_mask``: an additive mask broadcastable to [B, Hq, Nq, Nk] (for
+    example the [B, 1, 1, Nk] key-padding mask), added to the scaled scores;
+    -inf removes a key.  It is read in q's dtype; size-1 dims are broadcast
+    with stride 0.
     """
     torch = _torch()
     _require_gpu(q, k, v)
@@ -162,6 +188,7 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     sk = _seqlens(seqlens_k, B, dev)
     al = _slopes(alibi_slopes, Hq, dev)
     rope = _rope(rope_cos, rope_sin, rotary_dim, dev)
+    mask = _mask(attn_mask, q.dtype, (B, Hq, Nq, Nk), dev)
     p = _lib.PrefillParams()
     p.dtype = _dtype_code(q)
     p.batch, p.seqlen_q, p.seqlen_k = B, Nq, Nk
@@ -178,6 +205,9 @@ def prefill(q, k, v, *, causal: bool = False, window: int = -1, scale: Optional[
     p.v_stride[:] = [v.stride(0), v.stride(1), v.stride(2)]
     p.o_stride[:] = [out.stride(0), out.stride(1), out.stride(2)]
     p.alibi_slopes = al.data_ptr() if al is not None else None
+    if mask is not None:
+        p.attn_mask = mask.data_ptr()
+        p.mask_stride[:] = list(mask.stride())
     if rope is not None:
         p.rope_cos, p.rope_sin = rope[0].data_ptr(), rope[1].data_ptr()
         p.rotary_dim, p.rope_max_pos = rope[2], rope[3]

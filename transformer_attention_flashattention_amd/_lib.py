@@ -63,6 +63,8 @@ class PrefillParams(ctypes.Structure):
         ("rope_max_pos", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64),
+        ("attn_mask", ctypes.c_void_p),
+        ("mask_stride", ctypes.c_int64 * 4),
     ]
 
 

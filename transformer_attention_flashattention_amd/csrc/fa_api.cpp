@@ -212,6 +212,10 @@ fa_status validate_prefill(const fa_prefill_params *p) {
         return fail(FA_ERR_UNSUPPORTED, "k_stride[1] and v_stride[1] must be below 2^25 elements for bf16");
     FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
                       p->seqlen_k, false));
+    if (p->attn_mask) {
+        if (p->mask_stride[3] != 1) return fail(FA_ERR_UNSUPPORTED, "mask_stride[3] must be 1");
+        FA_TRY(check_strides("mask", p->mask_stride, 3, vec));
+    }
     // the K rotation pass puts batch and KV head on the second and third grid axes
     if (p->rotary_dim > 0 && p->dtype == FA_DTYPE_BF16 && (p->batch > 65535 || p->heads_kv > 65535))
         return fail(FA_ERR_UNSUPPORTED, "RoPE with bf16 supports batch and heads_kv up to 65535");
@@ -254,6 +258,8 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
         return fail(FA_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
     FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
                       p->seqlen_k, true));
+    if (p->attn_mask && !aligned16(p->attn_mask))
+        return fail(FA_ERR_UNSUPPORTED, "attn_mask must be 16-byte aligned");
     const size_t ws_need = prefill_ws_bytes(p);
     if (ws_need > 0 && p->seqlen_k > 0) {
         if (!p->workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", ws_need);
@@ -279,6 +285,8 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     if (p->rotary_dim > 0) {
         a.rope_cos = p->rope_cos; a.rope_sin = p->rope_sin; a.rotary_dim = p->rotary_dim;
     }
+    a.mask = p->attn_mask;
+    a.m_sb = p->mask_stride[0]; a.m_sh = p->mask_stride[1]; a.m_ss = p->mask_stride[2];
     const int bm = p->dtype == FA_DTYPE_BF16 ? fa::kPrefillBM : fa::kPrefillF32BM;
     a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
     if ((int64_t)a.num_q_tiles * a.heads_q * a.batch > 0x7fffffffLL)

@@ -27,6 +27,8 @@ struct PrefillArgs {
     const float *alibi;            // ALiBi slopes [heads_q] or null
     const float *rope_cos, *rope_sin;  // RoPE tables [max_pos, rotary_dim / 2], or null
     int32_t rotary_dim;            // 0 = no RoPE
+    const void *mask;              // additive mask (dtype of q), or null
+    int64_t m_sb, m_sh, m_ss;      // mask element strides: batch, head, query row (key: 1)
 };
 
 // K rotation pass (bf16 prefill with RoPE): rows j < Lk of every KV head,

@@ -172,8 +172,9 @@ __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
 }
 
 // D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores;
-// ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated).
-template <int D, bool ALIBI, bool ROPE>
+// ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated);
+// MASK: add an explicit additive mask read from memory.
+template <int D, bool ALIBI, bool ROPE, bool MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
@@ -368,6 +369,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // scale_log2 * s): scale * s - m |pos - j| = scale * (s - (m / scale) |pos - j|)
     float alibi_raw = 0.f;
     if constexpr (ALIBI) alibi_raw = -a.alibi[h] / a.scale;
+    // explicit mask: this lane's query row (clamped into the tensor for the
+    // rows of a partial query tile, whose scores are never used), in raw
+    // score units (mask / scale)
+    const unsigned short *mrow = nullptr;
+    float inv_scale = 0.f;
+    if constexpr (MASK) {
+        mrow = (const unsigned short *)a.mask + b * a.m_sb + h * a.m_sh +
+               (int64_t)min(qi, a.seqlen_q - 1) * a.m_ss;
+        inv_scale = 1.f / a.scale;
+    }
 
     // matrix step of tile j: PV of tile j-1 (from vb), then S of tile j (from kb).
     // Operand reads are issued in the order the MFMAs consume them and the
@@ -447,6 +458,32 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) {
                     const float dist = fabsf(base - (float)(sb * 32 + ((r >> 3) << 4) + (r & 7)));
                     s[sb][r] = __builtin_fmaf(dist, alibi_raw, s[sb][r]);
+                }
+        }
+        if constexpr (MASK) {
+            // the lane's keys are four runs of 8: k0 + 32 sb + 16 c + 8 half + e
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int key0 = k0 + sb * 32 + c * 16 + half * 8;
+                    float mv[8];
+                    if (key0 + 8 <= a.seqlen_k) {
+                        const u32x4 w = *(const u32x4 *)(mrow + key0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            mv[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+                            mv[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            mv[e] = key0 + e < a.seqlen_k
+                                        ? __builtin_bit_cast(float, (unsigned)mrow[key0 + e] << 16) : 0.f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        s[sb][c * 8 + e] = __builtin_fmaf(mv[e], inv_scale, s[sb][c * 8 + e]);
                 }
         }
         if (need_mask) {
@@ -566,30 +603,32 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
 }
 
+
+template <int D, bool ALIBI, bool ROPE>
+void launch_mask(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false>), grid, block, 0, s, a);
+}
+
+template <int D, bool ALIBI>
+void launch_rope(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.rotary_dim > 0) launch_mask<D, ALIBI, true>(a, grid, block, s);
+    else launch_mask<D, ALIBI, false>(a, grid, block, s);
+}
+
+template <int D>
+void launch_alibi(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.alibi) launch_rope<D, true>(a, grid, block, s);
+    else launch_rope<D, false>(a, grid, block, s);
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
     const dim3 grid((unsigned)a.num_q_tiles * a.heads_q * a.batch);
     const dim3 block(NTHREADS);
-    const bool alibi = a.alibi != nullptr;
-    const bool rope = a.rotary_dim > 0;
-    if (head_dim == 128) {
-        if (rope) {
-            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, true>), grid, block, 0, s, a);
-        } else {
-            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, false>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, false>), grid, block, 0, s, a);
-        }
-    } else {
-        if (rope) {
-            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, true, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<64, false, true>), grid, block, 0, s, a);
-        } else {
-            if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, true, false>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<64, false, false>), grid, block, 0, s, a);
-        }
-    }
+    if (head_dim == 128) launch_alibi<128>(a, grid, block, s);
+    else launch_alibi<64>(a, grid, block, s);
     return hipGetLastError();
 }
 

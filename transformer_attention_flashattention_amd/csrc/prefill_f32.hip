@@ -93,6 +93,12 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
     const float c2 = a.scale_log2;
     // ALiBi in raw score units: scale * s + bias = scale * (s + bias / scale)
     const float alibi_raw = a.alibi ? -a.alibi[h] / a.scale : 0.f;
+    // explicit additive mask row of this lane's query (clamped into the
+    // tensor for rows of a partial tile), in raw score units
+    const float *mrow = a.mask ? (const float *)a.mask + b * a.m_sb + h * a.m_sh +
+                                     (int64_t)min(qi, a.seqlen_q - 1) * a.m_ss
+                               : nullptr;
+    const float inv_scale = 1.f / a.scale;
 
     for (int t = t_begin; t < t_end; ++t) {
         const int k0 = t * BN;
@@ -132,6 +138,7 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
             if (a.causal) vis = vis && key <= pos;
             if (W > 0) vis = vis && key > pos - W;
             if (a.alibi) s[j] = __builtin_fmaf(fabsf((float)(pos - key)), alibi_raw, s[j]);
+            if (mrow && key < a.seqlen_k) s[j] = __builtin_fmaf(mrow[key], inv_scale, s[j]);
             s[j] = vis ? s[j] : -INFINITY;
             mx = fmaxf(mx, s[j]);
         }
