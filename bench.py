@@ -14,9 +14,9 @@ library), so the per-call averages are kernel time plus launch gaps.
 After the timed steps, the same two calls are timed with ALiBi slopes
 (reported under "alibi"), and the decode call over the same logical cache
 held in a paged pool of 16-row pages in shuffled order (under "paged") and
-as FP8 E4M3 codes with per-KV-head scales (under "fp8_kv"), and the prefill
-with RoPE over all 128 dims (under "rope"); none of these is part of the
-step.
+as FP8 E4M3 codes with per-KV-head scales (under "fp8_kv"), the prefill
+with RoPE over all 128 dims (under "rope") and with an explicit [1, 1, 1, N]
+additive mask (under "attn_mask"); none of these is part of the step.
 
 Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
 algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
@@ -240,6 +240,19 @@ def main():
     pre_r = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_r]))
     del wsr, rc, rs
 
+    # the prefill with an explicit [1, 1, 1, N] additive mask (all zero: the
+    # cost of reading a key-padding mask, the BERT page's layout)
+    mzero = torch.zeros((1, 1, 1, N), dtype=torch.bfloat16, device=dev)
+    fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse, attn_mask=mzero)
+    torch.cuda.synchronize()
+    ev_m = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_alibi)]
+    for e in ev_m:
+        e[0].record()
+        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse, attn_mask=mzero)
+        e[1].record()
+    torch.cuda.synchronize()
+    pre_m = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_m]))
+
     # the decode over a paged pool holding the same logical cache
     page = 16
     pp = workloads.make_workload_paged(5, page)
@@ -330,6 +343,8 @@ def main():
         "rope": {"rotary_dim": d, "prefill_ms_mean": round(pre_r, 4),
                  "prefill_tflops": round(flops / (pre_r * 1e-3) / 1e12, 2),
                  "note": "K rotation pass + attention with Q rotated at load", "calls": n_alibi},
+        "attn_mask": {"shape": [1, 1, 1, N], "prefill_ms_mean": round(pre_m, 4),
+                      "prefill_tflops": round(flops / (pre_m * 1e-3) / 1e12, 2), "calls": n_alibi},
         "fp8_kv": {"format": "e4m3", "decode_ms_mean": round(dec_f, 4),
                    "decode_gbs": round(fp8_bytes / (dec_f * 1e-3) / 1e9, 1),
                    "frac_of_hbm_peak": round(fp8_bytes / (dec_f * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
