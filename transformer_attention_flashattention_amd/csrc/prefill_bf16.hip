@@ -385,7 +385,34 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // schedule keeps the reads a few MFMAs ahead, so LDS latency hides under
     // matrix work instead of stalling every MFMA; consecutive MFMAs use
     // different accumulators.
+    // Explicit mask of tile j: loaded at the start of the wavefront's matrix
+    // step of tile j, so the loads are in flight during it and have landed
+    // by its softmax step (the next step of the same wavefront).  Keys at or
+    // beyond seqlen_k are never read.
+    u32x4 mpre[2][2];
+    auto prefetch_mask = [&](int j) __attribute__((always_inline)) {
+        if constexpr (MASK) {
+            const int k0 = (t_begin + tile_of(j)) * BN;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int key0 = k0 + sb * 32 + c * 16 + half * 8;
+                    if (key0 + 8 <= a.seqlen_k) {
+                        mpre[sb][c] = *(const u32x4 *)(mrow + key0);
+                    } else {
+                        u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (key0 + e < a.seqlen_k)
+                                w[e >> 1] |= (unsigned)mrow[key0 + e] << (16 * (e & 1));
+                        mpre[sb][c] = w;
+                    }
+                }
+        }
+    };
     auto matrix_step = [&](int j, const char *kb, const char *vb) {
+        if (j >= w_lo && j < w_hi) prefetch_mask(j);
         if (j - 1 >= w_lo && j - 1 < w_hi) {
             bf16x8 vf[4][DBLK];
 #pragma unroll
@@ -462,29 +489,19 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
         if constexpr (MASK) {
             // the lane's keys are four runs of 8: k0 + 32 sb + 16 c + 8 half + e
+            // (prefetched in the matrix step; keys past seqlen_k hold 0)
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int key0 = k0 + sb * 32 + c * 16 + half * 8;
-                    float mv[8];
-                    if (key0 + 8 <= a.seqlen_k) {
-                        const u32x4 w = *(const u32x4 *)(mrow + key0);
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            mv[2 * e] = __builtin_bit_cast(float, w[e] << 16);
-                            mv[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            mv[e] = key0 + e < a.seqlen_k
-                                        ? __builtin_bit_cast(float, (unsigned)mrow[key0 + e] << 16) : 0.f;
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned w = mpre[sb][c][e];
+                        s[sb][c * 8 + 2 * e] = __builtin_fmaf(__builtin_bit_cast(float, w << 16), inv_scale,
+                                                              s[sb][c * 8 + 2 * e]);
+                        s[sb][c * 8 + 2 * e + 1] = __builtin_fmaf(__builtin_bit_cast(float, w & 0xffff0000u),
+                                                                  inv_scale, s[sb][c * 8 + 2 * e + 1]);
                     }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        s[sb][c * 8 + e] = __builtin_fmaf(mv[e], inv_scale, s[sb][c * 8 + e]);
-                }
         }
         if (need_mask) {
 #pragma unroll
