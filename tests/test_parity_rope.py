@@ -144,3 +144,42 @@ def test_rope_decode(kind):
                                    window_left=200, rope_q=rope)
             ro[b], rl[b] = ob[0], lb[0]
     check(o, lse, ro, rl, "bf16", f"decode RoPE {kind}")
+
+
+def test_rope_k_pass_writes_only_its_workspace():
+    """The K rotation pass writes the valid rows of its workspace and nothing
+    around it; the workspace rows past a sequence's key length stay as they
+    were (the attention kernel never reads them)."""
+    p = workloads.make_prefill(130, 2, 200, 200, 4, 2, 128, "bf16", causal=True,
+                               seqlens_k_range=(50, 200), seqlens_q_equal_k=True)
+    cos_t, sin_t = tables(200, 128)
+    c, s = torch.from_numpy(cos_t).to(DEV), torch.from_numpy(sin_t).to(DEV)
+    q, k, v, sq, sk = prefill_inputs(p)
+    need = fa.prefill_workspace_size(q, k, rope_cos=c, rope_sin=s)
+    assert need == 2 * 200 * 2 * 128 * 2
+    pad = 4096
+    buf = torch.full((need + 2 * pad,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = buf[pad:pad + need]
+    say("[rope] K pass canaries")
+    o, lse = fa.prefill(q, k, v, causal=True, scale=p.scale, seqlens_q=sq, seqlens_k=sk,
+                        rope_cos=c, rope_sin=s, workspace=ws)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:pad] == 0xA5) and np.all(host[pad + need:] == 0xA5)
+    rows = host[pad:pad + need].view(np.uint16).reshape(2, 200, 2, 128)
+    for b in range(2):
+        L = int(p.seqlens_k[b])
+        assert np.all(rows[b, L:] == 0xA5A5)          # untouched past the valid length
+        want = oracle.rope_rotate(workloads.to_f64(p.k[b, :L].reshape(L * 2, 128), "bf16"),
+                                  np.repeat(np.arange(L), 2), cos_t, sin_t, 128, "bf16")
+        got = workloads.bf16_bits_to_f32(rows[b, :L].reshape(L * 2, 128)).astype(np.float64)
+        # the kernel rounds x c - y s computed in fp32, the oracle the exact value: at
+        # most one bf16 step apart, and equal almost everywhere
+        step = np.abs(want) * 2.0 ** -7 + 1e-30
+        assert np.all(np.abs(got - want) <= step)
+        assert np.mean(got == want) > 0.99
+    ro, rl = oracle.attention(workloads.to_f64(p.q, "bf16"), workloads.to_f64(p.k, "bf16"),
+                              workloads.to_f64(p.v, "bf16"), scale=p.scale, causal=True,
+                              seqlens_q=p.seqlens_q, seqlens_k=p.seqlens_k,
+                              rope=(cos_t, sin_t, 128, "bf16"))
+    check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "RoPE canaries")
