@@ -149,3 +149,12 @@ def test_alibi_decode_window_and_d64():
     o, lse = run_decode(dp, alibi_slopes=slopes)
     ro, rl = oracle_decode(dp, alibi_slopes=slopes)
     check(o, lse, ro, rl, dp.dtype, "ALiBi decode window d64")
+
+
+def test_long_cache_many_chunks():
+    """One sequence of 60000 keys in 128-key chunks: 469 partials, combined in
+    many rounds of the combine kernel."""
+    dp = workloads.make_decode(161, 2, 8, 2, 128, 60000, (1, 60000), "bf16",
+                               lengths=np.array([60000, 33333], dtype=np.int32))
+    _case(dp, "long cache, 128-key chunks", chunk_keys=128)
+    _case(dp, "long cache, library chunks")

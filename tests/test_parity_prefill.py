@@ -325,3 +325,11 @@ def test_alibi_causal_8k_sampled():
     o, lse = run_prefill(p, alibi_slopes=slopes)
     ro, rl = oracle_prefill(p, rows=rows, heads=heads, alibi_slopes=slopes)
     check(o[:, rows][:, :, heads], lse[:, heads][:, :, rows], ro, rl, p.dtype, "ALiBi 8k sampled")
+
+
+def test_long_sequence_sampled_rows():
+    """N = 40000 (not a tile multiple) on one head: long key ranges and large
+    row indices, sampled rows against the oracle."""
+    p = workloads.make_prefill(160, 1, 40000, 40000, 1, 1, 128, "bf16", causal=True)
+    rows = np.array([0, 1, 255, 256, 20000, 39743, 39744, 39998, 39999])
+    _sampled(p, "causal N40000 H1", rows, np.array([0]))
