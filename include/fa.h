@@ -55,7 +55,10 @@ typedef enum {
 
 typedef enum {
     FA_DTYPE_F32 = 0,         /* fp32 in, fp32 products and accumulation, fp32 out  */
-    FA_DTYPE_BF16 = 1         /* bf16 in, bf16 MFMA with fp32 accumulation, bf16 out */
+    FA_DTYPE_BF16 = 1,        /* bf16 in, bf16 MFMA with fp32 accumulation, bf16 out */
+    FA_DTYPE_F16 = 2          /* IEEE half in, half MFMA / dot products with fp32
+                                 accumulation, half out (the FP16 of the pages'
+                                 BERT benchmark)                                    */
 } fa_dtype;
 
 /* Storage of a decode KV cache (fa_decode_params.kv_format). */
@@ -129,7 +132,7 @@ typedef enum {
  * key-padding mask is strides {n, 0, 0, 1}); mask_stride[3] must be 1.  The
  * value is added to softmax_scale * q_i . k_j (after ALiBi, before the
  * implicit masks); -inf removes the key.  Pointer 16-byte aligned;
- * mask_stride[0..2] multiples of 8 elements (bf16) or 4 (fp32).  Values
+ * mask_stride[0..2] multiples of 8 elements (bf16, f16) or 4 (fp32).  Values
  * are read on the device and not validated.  The implicit masks stay the
  * cheap way to express causal, window and padding: an explicit mask adds
  * its bytes to every query tile's traffic.
@@ -138,8 +141,8 @@ typedef enum {
  * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
  * window_left == -1 or >= 1; extents >= 0; seqlens arrays (if given) are
  * device int32 [batch].  Pointers must be 16-byte aligned and strides of
- * batch/seq/head multiples of 8 elements (bf16) or 4 elements (fp32); for
- * bf16 the seq strides of k and v must be below 2^25 elements.  A request
+ * batch/seq/head multiples of 8 elements (bf16, f16) or 4 elements (fp32);
+ * for bf16 and f16 the seq strides of k and v must be below 2^25 elements.  A request
  * outside these limits returns FA_ERR_UNSUPPORTED or FA_ERR_INVALID_ARG
  * without launching anything.
  */
@@ -241,11 +244,12 @@ typedef struct {
  * decode cache holds keys already rotated at their own positions, written
  * when each token was appended.  rope_max_pos >= cache_capacity.
  *
- * Requirements: dtype FA_DTYPE_BF16; head_dim in {64, 128};
+ * Requirements: dtype FA_DTYPE_BF16 or FA_DTYPE_F16 (q, o and a plain
+ * cache); head_dim in {64, 128};
  * heads_q % heads_kv == 0; cache_capacity >= 1; softmax_scale finite and > 0.
  */
 typedef struct {
-    int32_t dtype;                       /* fa_dtype (bf16 only)                 */
+    int32_t dtype;                       /* fa_dtype (bf16 or f16)               */
     int32_t batch;
     int32_t heads_q;
     int32_t heads_kv;
@@ -311,7 +315,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10500
+#define FA_ABI_VERSION 10600
 
 #ifdef __cplusplus
 }

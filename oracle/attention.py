@@ -132,14 +132,17 @@ def alibi_bias(rows: np.ndarray, Nk: int, Lq: int, Lk: int, slope: float) -> np.
 
 
 def round_to_dtype(x: np.ndarray, dtype: Optional[str]) -> np.ndarray:
-    """Round float64 values to the nearest bf16 or fp32 value (ties to even),
-    returned as float64; ``dtype=None`` leaves them unrounded.  bf16: the
-    significand is scaled to 8 bits and rounded by ``rint`` (half to even)."""
+    """Round float64 values to the nearest bf16, half ("f16") or fp32 value
+    (ties to even), returned as float64; ``dtype=None`` leaves them
+    unrounded.  bf16: the significand is scaled to 8 bits and rounded by
+    ``rint`` (half to even); half and fp32 by NumPy's casts."""
     x = np.asarray(x, dtype=np.float64)
     if dtype is None:
         return x.copy()
     if dtype == "f32":
         return x.astype(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float64)
     if dtype != "bf16":
         raise ValueError(f"unknown dtype {dtype!r}")
     m, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1

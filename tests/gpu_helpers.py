@@ -2,7 +2,7 @@
 oracle calls on the same bits, and the tolerance checks.
 
 Tolerances (element-wise against the fp64 oracle):
-* bf16 inputs: max |dO| <= 2e-2 and mean |dO| <= 2e-3 over all of O; these
+* bf16 and half (f16) inputs: max |dO| <= 2e-2 and mean |dO| <= 2e-3 over all of O; these
   are the method's stated bounds.  LSE: max |dLSE| <= 1e-3 -- the scores
   themselves are exact products of bf16 values accumulated in fp32, so LSE
   only carries fp32 rounding (~1e-6 relative); 1e-3 leaves a wide margin
@@ -21,6 +21,7 @@ DEV = torch.device("cuda:0")
 
 TOL = {
     "bf16": dict(max=2e-2, mean=2e-3, lse=1e-3),
+    "f16": dict(max=2e-2, mean=2e-3, lse=1e-3),
     "f32": dict(max=1e-4, mean=1e-4, lse=1e-4),
 }
 
@@ -32,6 +33,8 @@ def say(msg):
 def dev_tensor(a, dtype):
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(DEV)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
@@ -99,8 +102,12 @@ def run_decode(dp, **kw):
 
 
 def _exact_f32(a, dtype):
-    # bf16 -> fp32 is exact; the oracle widens each slice it reads to fp64
-    return workloads.bf16_bits_to_f32(a) if dtype == "bf16" else a
+    # bf16 / half -> fp32 is exact; the oracle widens each slice it reads to fp64
+    if dtype == "bf16":
+        return workloads.bf16_bits_to_f32(a)
+    if dtype == "f16":
+        return np.ascontiguousarray(a).view(np.float16).astype(np.float32)
+    return a
 
 
 def oracle_decode(dp, batches=None, alibi_slopes=None):

@@ -189,6 +189,8 @@ def test_prefill_workspace_size(lib):
     assert _lib.prefill_workspace_size(p) == (_lib.FA_OK, 2 * 100 * 2 * 128 * 2)
     p = _prefill(dtype=_lib.FA_DTYPE_F32, rotary_dim=64, rope_max_pos=100)
     assert _lib.prefill_workspace_size(p) == (_lib.FA_OK, 0)
+    p = _prefill(dtype=_lib.FA_DTYPE_F16, rotary_dim=64, rope_max_pos=100)
+    assert _lib.prefill_workspace_size(p) == (_lib.FA_OK, 2 * 100 * 2 * 128 * 2)
     p = _prefill(rotary_dim=12, rope_max_pos=100)
     assert _lib.prefill_workspace_size(p)[0] == _lib.FA_ERR_UNSUPPORTED
     p = _prefill(batch=70000, rotary_dim=64, rope_max_pos=100)
@@ -389,3 +391,15 @@ def test_decode_fp8_strides_and_offsets(lib):
     assert "4 GiB" in _lib.last_error()
     st, n = _lib.decode_workspace_size(_decode(**big, **base))
     assert st == _lib.FA_OK and n > 0
+
+
+def test_half_dtype_rules(lib):
+    # half takes the 16-bit rules: strides in multiples of 8 elements, seq
+    # strides below 2^25; decode accepts it, and fp32 decode stays unsupported
+    p = _prefill(dtype=_lib.FA_DTYPE_F16, q_stride=[100 * 8 * 128, 8 * 128, 132])
+    assert _lib.prefill_fwd(p, 0) == _lib.FA_ERR_UNSUPPORTED
+    p = _prefill(dtype=_lib.FA_DTYPE_F16, k_stride=[1 << 30, 1 << 25, 128])
+    assert _lib.prefill_fwd(p, 0) == _lib.FA_ERR_UNSUPPORTED and "2^25" in _lib.last_error()
+    assert _lib.decode_workspace_size(_decode(dtype=_lib.FA_DTYPE_F16))[0] == _lib.FA_OK
+    assert _lib.decode_workspace_size(_decode(dtype=_lib.FA_DTYPE_F32))[0] == _lib.FA_ERR_UNSUPPORTED
+    assert _lib.decode_workspace_size(_decode(dtype=3))[0] == _lib.FA_ERR_INVALID_ARG

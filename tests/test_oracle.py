@@ -802,6 +802,11 @@ def test_round_to_dtype_single_rounding_to_nearest_even():
     assert np.array_equal(oracle.round_to_dtype(x.astype(np.float64), "bf16"), ref)
     y = np.random.default_rng(4).standard_normal(1000)
     assert np.array_equal(oracle.round_to_dtype(y, "f32"), y.astype(np.float32).astype(np.float64))
+    # half: against torch's float16 cast of fp32 values, and a tie going to even
+    xh = np.random.default_rng(6).standard_normal(50000).astype(np.float32) * 30
+    refh = torch.from_numpy(xh).to(torch.float16).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.round_to_dtype(xh.astype(np.float64), "f16"), refh)
+    assert oracle.round_to_dtype(np.array([1.0 + 2.0 ** -11]), "f16")[0] == 1.0
     assert np.array_equal(oracle.round_to_dtype(y, None), y)
 
 
@@ -852,3 +857,12 @@ def test_mask_matches_torch_sdpa_float_mask():
     np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
     s = float(np.float32(0.35)) * np.einsum("bqhd,bkhd->bhqk", q, k) + mask
     np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_half_storage_matches_torch():
+    x = np.random.default_rng(9).standard_normal(20000).astype(np.float32) * 50
+    bits = workloads._store(x, "f16")
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, ref)
+    assert np.array_equal(workloads.to_f64(bits, "f16"),
+                          torch.from_numpy(ref.view(np.int16)).view(torch.float16).double().numpy())

@@ -41,9 +41,11 @@ def _dtype_code(t) -> int:
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return _lib.FA_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return _lib.FA_DTYPE_F16
     if t.dtype == torch.float32:
         return _lib.FA_DTYPE_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _require_gpu(*tensors):

@@ -22,6 +22,7 @@ FA_ERR_HIP = 4
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 FA_KV_PLAIN = 0
 FA_KV_FP8_E4M3 = 1
 

@@ -41,6 +41,7 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
@@ -148,20 +149,56 @@ __device__ __forceinline__ T load_nt(const char *base, unsigned off) {
     return __builtin_nontemporal_load((const T *)(base + off));
 }
 
-// Two FP8 E4M3 codes (bytes 0-1 of w, or bytes 2-3 with HI) as a bf16 pair.
-// Every E4M3 value is exact in bf16, so this loses nothing.
-template <bool HI>
-__device__ __forceinline__ unsigned e4m3x2_to_bf16x2(unsigned w) {
-    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
+// The 16-bit type of q, o and of P in the P.V products: bf16, or IEEE half
+// with F16.  Pairs of values travel packed in one 32-bit register.
+template <bool F16> struct H16;
+template <> struct H16<false> {
+    using t = __bf16;
+    static __device__ __forceinline__ unsigned pack(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    static __device__ __forceinline__ float dot(unsigned a, unsigned b, float c) { return dot2(a, b, c); }
+    static __device__ __forceinline__ float lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+    static __device__ __forceinline__ float hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+    // two FP8 E4M3 codes (bytes 0-1 of w, or 2-3 with HI) as a pair; every
+    // E4M3 value is exact in bf16
+    template <bool HI>
+    static __device__ __forceinline__ unsigned from_e4m3(unsigned w) {
+        return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    }
+};
+template <> struct H16<true> {
+    using t = _Float16;
+    static __device__ __forceinline__ unsigned pack(float lo, float hi) {
+        f16x2 r;
+        r[0] = (_Float16)lo;
+        r[1] = (_Float16)hi;
+        return __builtin_bit_cast(unsigned, r);
+    }
+    static __device__ __forceinline__ float dot(unsigned a, unsigned b, float c) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+    }
+    static __device__ __forceinline__ float lo(unsigned w) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(unsigned w) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+    }
+    // every E4M3 value is exact in half too (normal range 2^-6 .. 448,
+    // subnormals down to 2^-9)
+    template <bool HI>
+    static __device__ __forceinline__ unsigned from_e4m3(unsigned w) {
+        return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    }
+};
 
 // D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
 // a slice of it); ALIBI: add the per-head linear bias -m (L - 1 - j); PAGED:
 // the cache is a pool of pages named by a block table; KV8: K and V are FP8
 // E4M3 codes with one scale per KV head each.  Chunk lengths are multiples of
-// NWAVES * KT.  KT: keys per wavefront tile.
-template <int D, int GT, bool ALIBI, bool PAGED, bool KV8, int KT>
+// NWAVES * KT.  KT: keys per wavefront tile.  F16: q and o are IEEE half
+// (and so is P in the P.V products) instead of bf16.
+template <int D, int GT, bool ALIBI, bool PAGED, bool KV8, int KT, bool F16>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
+    using H = H16<F16>;
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
     constexpr int SKP = 64 / SL;             // keys per score pass
     constexpr int SP = KT / SKP;             // score passes per tile
@@ -270,9 +307,8 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 const float c = cr[pr], sn = sr[pr];
 #pragma unroll
                 for (int g = 0; g < GT; ++g) {
-                    const bf16x2 v = __builtin_bit_cast(bf16x2, qr[g][k]);
-                    const float x = (float)v[0], y = (float)v[1];
-                    qr[g][k] = pack_bf16x2(__builtin_fmaf(x, c, -y * sn), __builtin_fmaf(x, sn, y * c));
+                    const float x = H::lo(qr[g][k]), y = H::hi(qr[g][k]);
+                    qr[g][k] = H::pack(__builtin_fmaf(x, c, -y * sn), __builtin_fmaf(x, sn, y * c));
                 }
             }
         }
@@ -365,8 +401,8 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (KV8) {
-                    kw[2 * i] = e4m3x2_to_bf16x2<false>(kt[p][0][i]);
-                    kw[2 * i + 1] = e4m3x2_to_bf16x2<true>(kt[p][0][i]);
+                    kw[2 * i] = H::template from_e4m3<false>(kt[p][0][i]);
+                    kw[2 * i + 1] = H::template from_e4m3<true>(kt[p][0][i]);
                 } else {
                     kw[i] = kt[p][0][i];
                     kw[4 + i] = kt[p][KPC - 1][i];
@@ -376,7 +412,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             for (int g = 0; g < GT; ++g) {
                 float acc = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = dot2(kw[i], qr[g][i], acc);
+                for (int i = 0; i < 8; ++i) acc = H::dot(kw[i], qr[g][i], acc);
                 acc = group_sum<SL>(acc);
                 if constexpr (KV8) acc *= k_scale;
                 if constexpr (ALIBI) acc = __builtin_fmaf((float)(L - 1 - j), alibi_raw[g], acc);
@@ -449,16 +485,16 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             }
             unsigned pp[GT];
 #pragma unroll
-            for (int g = 0; g < GT; ++g) pp[g] = pack_bf16x2(pa[g], pb[g]);
+            for (int g = 0; g < GT; ++g) pp[g] = H::pack(pa[g], pb[g]);
             // this lane's 8 dims of keys p and p + 1 as bf16 pairs
             unsigned wa[4], wb[4];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if constexpr (KV8) {
-                    wa[2 * i] = e4m3x2_to_bf16x2<false>(vt[p][i]);
-                    wa[2 * i + 1] = e4m3x2_to_bf16x2<true>(vt[p][i]);
-                    wb[2 * i] = e4m3x2_to_bf16x2<false>(vt[p + 1][i]);
-                    wb[2 * i + 1] = e4m3x2_to_bf16x2<true>(vt[p + 1][i]);
+                    wa[2 * i] = H::template from_e4m3<false>(vt[p][i]);
+                    wa[2 * i + 1] = H::template from_e4m3<true>(vt[p][i]);
+                    wb[2 * i] = H::template from_e4m3<false>(vt[p + 1][i]);
+                    wb[2 * i + 1] = H::template from_e4m3<true>(vt[p + 1][i]);
                 } else {
                     wa[2 * i] = vt[p][2 * i];
                     wa[2 * i + 1] = vt[p][2 * i + 1];
@@ -473,8 +509,8 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 const unsigned odd = __builtin_amdgcn_perm(vb, va, 0x07060302u);   // (va.hi, vb.hi)
 #pragma unroll
                 for (int g = 0; g < GT; ++g) {
-                    o[g][2 * i] = dot2(pp[g], even, o[g][2 * i]);
-                    o[g][2 * i + 1] = dot2(pp[g], odd, o[g][2 * i + 1]);
+                    o[g][2 * i] = H::dot(pp[g], even, o[g][2 * i]);
+                    o[g][2 * i + 1] = H::dot(pp[g], odd, o[g][2 * i + 1]);
                 }
             }
         }
@@ -555,7 +591,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
 constexpr int COMBINE_THREADS = 256;
 constexpr int COMBINE_GROUP = 8;     // partial rows loaded per round trip
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeArgs a) {
     constexpr int DPL = D / 64;              // dims per lane
     const int lane = threadIdx.x & 63;
@@ -608,7 +644,7 @@ __global__ __launch_bounds__(COMBINE_THREADS) void decode_combine_kernel(DecodeA
     unsigned short *orow = (unsigned short *)a.o + b * a.o_sb + h * a.o_sh + lane * DPL;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
-        const __bf16 x = (__bf16)(acc[i] * inv);
+        const typename H16<F16>::t x = (typename H16<F16>::t)(acc[i] * inv);
         orow[i] = __builtin_bit_cast(unsigned short, x);
     }
     if (a.lse && lane == 0)
@@ -621,53 +657,57 @@ int tile_keys(const DecodeArgs &a) {
     return (a.kv_fp8 && (!a.block_table || a.page_size % 32 == 0)) ? 32 : 16;
 }
 
-template <int D, int GT, bool ALIBI, bool PAGED>
+template <int D, bool F16, int GT, bool ALIBI, bool PAGED>
 void launch_split_kv(const DecodeArgs &a, dim3 grid, hipStream_t s) {
     if (!a.kv_fp8)
-        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, false, 16>), grid, dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, false, 16, F16>), grid, dim3(NTHREADS), 0, s, a);
     else if (tile_keys(a) == 32)
-        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 32>), grid, dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 32, F16>), grid, dim3(NTHREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 16>), grid, dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 16, F16>), grid, dim3(NTHREADS), 0, s, a);
 }
 
-template <int D, int GT, bool ALIBI>
+template <int D, bool F16, int GT, bool ALIBI>
 void launch_split_paged(const DecodeArgs &a, dim3 grid, hipStream_t s) {
-    if (a.block_table) launch_split_kv<D, GT, ALIBI, true>(a, grid, s);
-    else launch_split_kv<D, GT, ALIBI, false>(a, grid, s);
+    if (a.block_table) launch_split_kv<D, F16, GT, ALIBI, true>(a, grid, s);
+    else launch_split_kv<D, F16, GT, ALIBI, false>(a, grid, s);
 }
 
-template <int D, int GT>
+template <int D, bool F16, int GT>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)(a.heads_kv * a.head_groups) * a.batch * a.max_chunks);
-    if (a.alibi) launch_split_paged<D, GT, true>(a, grid, s);
-    else launch_split_paged<D, GT, false>(a, grid, s);
+    if (a.alibi) launch_split_paged<D, F16, GT, true>(a, grid, s);
+    else launch_split_paged<D, F16, GT, false>(a, grid, s);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t launch_all(const DecodeArgs &a, int gt, hipStream_t s) {
     hipError_t e;
     switch (gt) {
-        case 1: e = launch_split<D, 1>(a, s); break;
-        case 2: e = launch_split<D, 2>(a, s); break;
-        default: e = launch_split<D, 4>(a, s); break;
+        case 1: e = launch_split<D, F16, 1>(a, s); break;
+        case 2: e = launch_split<D, F16, 2>(a, s); break;
+        default: e = launch_split<D, F16, 4>(a, s); break;
     }
     if (e != hipSuccess) return e;
     const int per_wg = COMBINE_THREADS / 64;
-    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((a.batch * a.heads_q + per_wg - 1) / per_wg),
-                       dim3(COMBINE_THREADS), 0,
-                       s, a);
+    hipLaunchKernelGGL((decode_combine_kernel<D, F16>), dim3((a.batch * a.heads_q + per_wg - 1) / per_wg),
+                       dim3(COMBINE_THREADS), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs &args, int head_dim, int heads_per_wg, hipStream_t s) {
+hipError_t launch_decode_bf16(const DecodeArgs &args, int head_dim, int heads_per_wg, bool f16,
+                              hipStream_t s) {
     DecodeArgs a = args;
     a.origin_align = a.block_table ? tile_keys(a) : 1;
-    if (head_dim == 128) return launch_all<128>(a, heads_per_wg, s);
-    return launch_all<64>(a, heads_per_wg, s);
+    if (f16) {
+        if (head_dim == 128) return launch_all<128, true>(a, heads_per_wg, s);
+        return launch_all<64, true>(a, heads_per_wg, s);
+    }
+    if (head_dim == 128) return launch_all<128, false>(a, heads_per_wg, s);
+    return launch_all<64, false>(a, heads_per_wg, s);
 }
 
 }  // namespace fa

@@ -97,9 +97,9 @@ int decode_chunk(const fa_decode_params *p, int gt) {
 
 fa_status validate_decode(const fa_decode_params *p) {
     if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
-    if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32)
+    if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_F16)
         return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-    if (p->dtype != FA_DTYPE_BF16) return fail(FA_ERR_UNSUPPORTED, "decode supports bf16 only");
+    if (p->dtype == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "decode supports bf16 and f16 only");
     if (p->batch < 0) return fail(FA_ERR_INVALID_ARG, "batch must be >= 0");
     if (p->heads_q <= 0 || p->heads_kv <= 0)
         return fail(FA_ERR_INVALID_ARG, "heads_q and heads_kv must be >= 1");
@@ -181,13 +181,13 @@ size_t decode_ws_bytes(const fa_decode_params *p, int chunk) {
 
 // Workspace of a prefill call: the rotated copy of K (bf16 with RoPE only).
 size_t prefill_ws_bytes(const fa_prefill_params *p) {
-    if (p->rotary_dim == 0 || p->dtype != FA_DTYPE_BF16) return 0;
+    if (p->rotary_dim == 0 || p->dtype == FA_DTYPE_F32) return 0;
     return (size_t)p->batch * p->seqlen_k * p->heads_kv * p->head_dim * 2;
 }
 
 fa_status validate_prefill(const fa_prefill_params *p) {
     if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
-    if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32)
+    if (p->dtype != FA_DTYPE_BF16 && p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_F16)
         return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
     if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
         return fail(FA_ERR_INVALID_ARG, "batch, seqlen_q and seqlen_k must be >= 0");
@@ -202,14 +202,15 @@ fa_status validate_prefill(const fa_prefill_params *p) {
     if (p->window_left == 0 || p->window_left < -1)
         return fail(FA_ERR_INVALID_ARG, "window_left must be -1 or >= 1 (got %d)", p->window_left);
     FA_TRY(check_scale(p->softmax_scale));
-    const int vec = p->dtype == FA_DTYPE_BF16 ? 8 : 4;
+    const bool half_width = p->dtype != FA_DTYPE_F32;  // bf16 or half
+    const int vec = half_width ? 8 : 4;
     FA_TRY(check_strides("q", p->q_stride, 3, vec));
     FA_TRY(check_strides("k", p->k_stride, 3, vec));
     FA_TRY(check_strides("v", p->v_stride, 3, vec));
     FA_TRY(check_strides("o", p->o_stride, 3, vec));
     // the bf16 kernel addresses the rows of one 64-key tile with 32-bit byte offsets
-    if (p->dtype == FA_DTYPE_BF16 && (p->k_stride[1] >= (1LL << 25) || p->v_stride[1] >= (1LL << 25)))
-        return fail(FA_ERR_UNSUPPORTED, "k_stride[1] and v_stride[1] must be below 2^25 elements for bf16");
+    if (half_width && (p->k_stride[1] >= (1LL << 25) || p->v_stride[1] >= (1LL << 25)))
+        return fail(FA_ERR_UNSUPPORTED, "k_stride[1] and v_stride[1] must be below 2^25 elements for bf16 / f16");
     FA_TRY(check_rope(p->rotary_dim, p->rope_max_pos, p->rope_cos, p->rope_sin, p->head_dim,
                       p->seqlen_k, false));
     if (p->attn_mask) {
@@ -217,8 +218,8 @@ fa_status validate_prefill(const fa_prefill_params *p) {
         FA_TRY(check_strides("mask", p->mask_stride, 3, vec));
     }
     // the K rotation pass puts batch and KV head on the second and third grid axes
-    if (p->rotary_dim > 0 && p->dtype == FA_DTYPE_BF16 && (p->batch > 65535 || p->heads_kv > 65535))
-        return fail(FA_ERR_UNSUPPORTED, "RoPE with bf16 supports batch and heads_kv up to 65535");
+    if (p->rotary_dim > 0 && half_width && (p->batch > 65535 || p->heads_kv > 65535))
+        return fail(FA_ERR_UNSUPPORTED, "RoPE with bf16 / f16 supports batch and heads_kv up to 65535");
     return FA_OK;
 }
 
@@ -287,7 +288,8 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     }
     a.mask = p->attn_mask;
     a.m_sb = p->mask_stride[0]; a.m_sh = p->mask_stride[1]; a.m_ss = p->mask_stride[2];
-    const int bm = p->dtype == FA_DTYPE_BF16 ? fa::kPrefillBM : fa::kPrefillF32BM;
+    const bool f16 = p->dtype == FA_DTYPE_F16;
+    const int bm = p->dtype != FA_DTYPE_F32 ? fa::kPrefillBM : fa::kPrefillF32BM;
     a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
     if ((int64_t)a.num_q_tiles * a.heads_q * a.batch > 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
@@ -300,15 +302,15 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
         r.k_sb = p->k_stride[0]; r.k_ss = p->k_stride[1]; r.k_sh = p->k_stride[2];
         r.batch = p->batch; r.seqlen_k = p->seqlen_k; r.heads_kv = p->heads_kv;
         r.rope_cos = p->rope_cos; r.rope_sin = p->rope_sin; r.rotary_dim = p->rotary_dim;
-        const hipError_t er = fa::launch_rope_k_bf16(r, p->head_dim, s);
+        const hipError_t er = fa::launch_rope_k_bf16(r, p->head_dim, f16, s);
         if (er != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(er));
         a.k = p->workspace;
         a.k_sb = (int64_t)p->seqlen_k * p->heads_kv * p->head_dim;
         a.k_ss = (int64_t)p->heads_kv * p->head_dim;
         a.k_sh = p->head_dim;
     }
-    const hipError_t e = p->dtype == FA_DTYPE_BF16 ? fa::launch_prefill_bf16(a, p->head_dim, s)
-                                                   : fa::launch_prefill_f32(a, p->head_dim, s);
+    const hipError_t e = p->dtype != FA_DTYPE_F32 ? fa::launch_prefill_bf16(a, p->head_dim, f16, s)
+                                                  : fa::launch_prefill_f32(a, p->head_dim, s);
     if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -371,7 +373,8 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     a.ws_o = static_cast<float *>(workspace);
     a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
 
-    const hipError_t e = fa::launch_decode_bf16(a, p->head_dim, gt, static_cast<hipStream_t>(hip_stream));
+    const hipError_t e = fa::launch_decode_bf16(a, p->head_dim, gt, p->dtype == FA_DTYPE_F16,
+                                                static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -71,10 +71,12 @@ struct DecodeArgs {
 };
 
 // Each launcher enqueues its kernel(s) and returns the launch status.
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
+// 16-bit prefill (bf16, or IEEE half when f16) and the K rotation pass
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool f16, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
-hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_wg,
+hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, bool f16, hipStream_t s);
+// decode with 16-bit q and o (bf16, or IEEE half when f16)
+hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_wg, bool f16,
                               hipStream_t s);
 
 // Tile sizes the launchers use (also needed by the host for grid sizing).

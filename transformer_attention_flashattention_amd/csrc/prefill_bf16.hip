@@ -80,6 +80,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -93,9 +95,6 @@ constexpr int NTHREADS = NWAVES * 64;
 static_assert(BM == NWAVES * 32, "one 32-row block per wavefront");
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 of the largest un-rescaled p
-// Fast-path bound on the P values of one lane's share of a tile: 2^16 keeps
-// bf16 P and the fp32 accumulators far from overflow.
-constexpr float FAST_BOUND = 65536.0f;
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
@@ -125,6 +124,52 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(unsigned, r);
 }
+
+// The 16-bit element type of Q, K, V, O (and of P in the P.V product):
+// bf16, or IEEE half with F16.  Both use the same 32x32x16 MFMA shape with
+// fp32 accumulation and the same operand layouts.
+template <bool F16> struct E16;
+template <> struct E16<false> {
+    using t = __bf16;
+    using v8 = bf16x8;
+    // fast-path bound on a lane's P sum (keeps every P far inside the type)
+    // fast-path bound on the P values of one lane's share of a tile: 2^16
+    // keeps bf16 P and the fp32 accumulators far from overflow
+    static constexpr float FAST_BOUND = 65536.0f;
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ unsigned pack(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    static __device__ __forceinline__ float lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+    static __device__ __forceinline__ float hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+    static __device__ __forceinline__ float one(unsigned short b) {
+        return __builtin_bit_cast(float, (unsigned)b << 16);
+    }
+};
+template <> struct E16<true> {
+    using t = _Float16;
+    using v8 = f16x8;
+    // half tops out at 65504: P sums stay at or below 2^14
+    static constexpr float FAST_BOUND = 16384.0f;
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ unsigned pack(float lo, float hi) {
+        f16x2 r;
+        r[0] = (_Float16)lo;
+        r[1] = (_Float16)hi;
+        return __builtin_bit_cast(unsigned, r);
+    }
+    static __device__ __forceinline__ float lo(unsigned w) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+    }
+    static __device__ __forceinline__ float hi(unsigned w) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+    }
+    static __device__ __forceinline__ float one(unsigned short b) {
+        return (float)__builtin_bit_cast(_Float16, b);
+    }
+};
 
 // Workgroup barrier of the phase loop.  __syncthreads() would also drain
 // every outstanding vector-memory operation of the wavefront (its fence is
@@ -173,12 +218,16 @@ __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
 
 // D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores;
 // ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated);
-// MASK: add an explicit additive mask read from memory.
-template <int D, bool ALIBI, bool ROPE, bool MASK>
+// MASK: add an explicit additive mask read from memory; F16: the inputs are
+// IEEE half instead of bf16.
+template <int D, bool ALIBI, bool ROPE, bool MASK, bool F16>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
     using T = Tile<D>;
+    using E = E16<F16>;
+    using v8 = typename E::v8;
+    using et = typename E::t;
     constexpr int KSTEPS = D / 16;        // MFMA k-steps over head_dim for S
     constexpr int DBLK = D / 32;          // 32-dim row blocks of O^T
 
@@ -254,7 +303,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int64_t k_row_bytes = a.k_ss * 2, v_row_bytes = a.v_ss * 2;
 
     // ---- Q fragment (B operand), zero for rows outside the valid length ---
-    bf16x8 qf[KSTEPS];
+    v8 qf[KSTEPS];
     {
         const bool ok = qi < Lq;
         const unsigned short *row = Qp + (int64_t)qi * a.q_ss + half * 8;
@@ -262,7 +311,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (ok) v = *(const u32x4 *)(row + ks * 16);
-            qf[ks] = __builtin_bit_cast(bf16x8, v);
+            qf[ks] = __builtin_bit_cast(v8, v);
         }
         // RoPE: the lane's 8 dims of a k-step are 4 adjacent pairs, turned by
         // the angles of its row's position (qi + Lk - Lq); the result is
@@ -282,8 +331,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float x = (float)qf[ks][2 * e], y = (float)qf[ks][2 * e + 1];
-                            qf[ks][2 * e] = (__bf16)__builtin_fmaf(x, cc[e], -y * ss[e]);
-                            qf[ks][2 * e + 1] = (__bf16)__builtin_fmaf(x, ss[e], y * cc[e]);
+                            qf[ks][2 * e] = (et)__builtin_fmaf(x, cc[e], -y * ss[e]);
+                            qf[ks][2 * e + 1] = (et)__builtin_fmaf(x, ss[e], y * cc[e]);
                         }
                     }
                 }
@@ -353,13 +402,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
     float m_ref = -INFINITY;   // reference row max, scaled log2 domain
     float l_run = 0.f;         // running row sum over this lane's keys
     f32x16 s[2];               // S^T of the tile in flight (matrix -> softmax step)
-    bf16x8 pb[4];              // P^T of the tile in flight (softmax -> matrix step)
+    v8 pb[4];                  // P^T of the tile in flight (softmax -> matrix step)
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(v8, u32x4{0u, 0u, 0u, 0u});
 
     const int pos = qi + offset;                     // key position of this row
     const float c2 = a.scale_log2;
@@ -414,7 +463,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     auto matrix_step = [&](int j, const char *kb, const char *vb) {
         if (j >= w_lo && j < w_hi) prefetch_mask(j);
         if (j - 1 >= w_lo && j - 1 < w_hi) {
-            bf16x8 vf[4][DBLK];
+            v8 vf[4][DBLK];
 #pragma unroll
             for (int ksp = 0; ksp < 4; ++ksp)
 #pragma unroll
@@ -426,13 +475,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
                             (__attribute__((address_space(3))) s16x4 *)(vb + v_off[jd] +
                                                                         (16 * ksp + 4 * tt) * T::ROWB));
                     vf[ksp][jd] = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                        v8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
                 }
 #pragma unroll
             for (int ksp = 0; ksp < 4; ++ksp)
 #pragma unroll
                 for (int jd = 0; jd < DBLK; ++jd)
-                    oacc[jd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksp][jd], pb[ksp], oacc[jd], 0, 0, 0);
+                    oacc[jd] = E::mfma(vf[ksp][jd], pb[ksp], oacc[jd]);
             // 2 DS reads per MFMA, kept 4 MFMAs ahead
             __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
 #pragma unroll
@@ -443,12 +492,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
         }
         if (j >= w_lo && j < w_hi) {
-            bf16x8 kf[KSTEPS][2];
+            v8 kf[KSTEPS][2];
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
-                    kf[ks][sb] = *(const bf16x8 *)(kb + sb * 32 * T::ROWB + k_off[ks]);
+                    kf[ks][sb] = *(const v8 *)(kb + sb * 32 * T::ROWB + k_off[ks]);
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -457,7 +506,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
             for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
-                    s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][sb], qf[ks], s[sb], 0, 0, 0);
+                    s[sb] = E::mfma(kf[ks][sb], qf[ks], s[sb]);
             // 1 DS read per MFMA, kept 4 MFMAs ahead
             __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
@@ -497,10 +546,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const unsigned w = mpre[sb][c][e];
-                        s[sb][c * 8 + 2 * e] = __builtin_fmaf(__builtin_bit_cast(float, w << 16), inv_scale,
-                                                              s[sb][c * 8 + 2 * e]);
-                        s[sb][c * 8 + 2 * e + 1] = __builtin_fmaf(__builtin_bit_cast(float, w & 0xffff0000u),
-                                                                  inv_scale, s[sb][c * 8 + 2 * e + 1]);
+                        s[sb][c * 8 + 2 * e] = __builtin_fmaf(E::lo(w), inv_scale, s[sb][c * 8 + 2 * e]);
+                        s[sb][c * 8 + 2 * e + 1] = __builtin_fmaf(E::hi(w), inv_scale, s[sb][c * 8 + 2 * e + 1]);
                     }
         }
         if (need_mask) {
@@ -524,10 +571,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
                     for (int i = 0; i < 4; ++i) {
                         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i], c2, -m_use));
                         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][tt * 8 + 2 * i + 1], c2, -m_use));
-                        w[i] = pack_bf16x2(p0, p1);
+                        w[i] = E::pack(p0, p1);
                         psum += p0 + p1;
                     }
-                    pb[sb * 2 + tt] = __builtin_bit_cast(bf16x8, w);
+                    pb[sb * 2 + tt] = __builtin_bit_cast(v8, w);
                 }
         };
         float psum;
@@ -537,7 +584,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         // overflow to inf).  Then the wavefront takes the exact row
         // max, moves the reference where it grew past the threshold, rescales
         // O and the row sum, and recomputes P.
-        if (__ballot(m_ref == -INFINITY || !(psum <= FAST_BOUND))) {
+        if (__ballot(m_ref == -INFINITY || !(psum <= E::FAST_BOUND))) {
             float mx = s[0][0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
@@ -609,8 +656,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
             for (int j = 0; j < 4; ++j) {
                 const int d = jd * 32 + j * 8 + half * 4;
                 u32x2 w;
-                w[0] = pack_bf16x2(oacc[jd][4 * j] * inv, oacc[jd][4 * j + 1] * inv);
-                w[1] = pack_bf16x2(oacc[jd][4 * j + 2] * inv, oacc[jd][4 * j + 3] * inv);
+                w[0] = E::pack(oacc[jd][4 * j] * inv, oacc[jd][4 * j + 1] * inv);
+                w[1] = E::pack(oacc[jd][4 * j + 2] * inv, oacc[jd][4 * j + 3] * inv);
                 *(u32x2 *)(orow + d) = w;
             }
         if (a.lse && half == 0) {
@@ -621,31 +668,36 @@ void prefill_bf16_kernel(PrefillArgs a) {
 }
 
 
-template <int D, bool ALIBI, bool ROPE>
+template <int D, bool F16, bool ALIBI, bool ROPE>
 void launch_mask(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-    if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false>), grid, block, 0, s, a);
+    if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16>), grid, block, 0, s, a);
 }
 
-template <int D, bool ALIBI>
+template <int D, bool F16, bool ALIBI>
 void launch_rope(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-    if (a.rotary_dim > 0) launch_mask<D, ALIBI, true>(a, grid, block, s);
-    else launch_mask<D, ALIBI, false>(a, grid, block, s);
+    if (a.rotary_dim > 0) launch_mask<D, F16, ALIBI, true>(a, grid, block, s);
+    else launch_mask<D, F16, ALIBI, false>(a, grid, block, s);
 }
 
-template <int D>
+template <int D, bool F16>
 void launch_alibi(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-    if (a.alibi) launch_rope<D, true>(a, grid, block, s);
-    else launch_rope<D, false>(a, grid, block, s);
+    if (a.alibi) launch_rope<D, F16, true>(a, grid, block, s);
+    else launch_rope<D, F16, false>(a, grid, block, s);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool f16, hipStream_t s) {
     const dim3 grid((unsigned)a.num_q_tiles * a.heads_q * a.batch);
     const dim3 block(NTHREADS);
-    if (head_dim == 128) launch_alibi<128>(a, grid, block, s);
-    else launch_alibi<64>(a, grid, block, s);
+    if (f16) {
+        if (head_dim == 128) launch_alibi<128, true>(a, grid, block, s);
+        else launch_alibi<64, true>(a, grid, block, s);
+    } else {
+        if (head_dim == 128) launch_alibi<128, false>(a, grid, block, s);
+        else launch_alibi<64, false>(a, grid, block, s);
+    }
     return hipGetLastError();
 }
 

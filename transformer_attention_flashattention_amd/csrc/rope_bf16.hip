@@ -1,4 +1,4 @@
-// Rotary position encoding of K for the bf16 prefill, for gfx950.
+// Rotary position encoding of K for the 16-bit (bf16 / half) prefill, for gfx950.
 //
 // RoPE (jsqmd.com ops-transformer practice page, section 三, rotary position
 // encoding): the vector at position m is rotated pair by pair; each pair of
@@ -17,22 +17,30 @@
 // written (the attention kernel never reads them either).
 #include "fa_internal.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
+// Rotate one adjacent pair held as two 16-bit values (bf16, or half with
+// F16), rounding the result back to that type.
+template <bool F16>
 __device__ __forceinline__ unsigned rotate_pair(unsigned xy, float c, float s) {
-    const bf16x2 v = __builtin_bit_cast(bf16x2, xy);
+    using v2 = typename std::conditional<F16, f16x2, bf16x2>::type;
+    using et = typename std::conditional<F16, _Float16, __bf16>::type;
+    const v2 v = __builtin_bit_cast(v2, xy);
     const float x = (float)v[0], y = (float)v[1];
-    bf16x2 r;
-    r[0] = (__bf16)__builtin_fmaf(x, c, -y * s);
-    r[1] = (__bf16)__builtin_fmaf(x, s, y * c);
+    v2 r;
+    r[0] = (et)__builtin_fmaf(x, c, -y * s);
+    r[1] = (et)__builtin_fmaf(x, s, y * c);
     return __builtin_bit_cast(unsigned, r);
 }
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void rope_k_bf16_kernel(RopeKArgs a) {
     constexpr int PIECES = D / 8;                        // 16-byte pieces per row
     constexpr int KEYS = 256 / PIECES;                   // key rows per workgroup
@@ -48,10 +56,10 @@ __global__ __launch_bounds__(256) void rope_k_bf16_kernel(RopeKArgs a) {
         const int half = a.rotary_dim / 2;
         const float4 c = *(const float4 *)(a.rope_cos + (int64_t)j * half + piece * 4);
         const float4 s = *(const float4 *)(a.rope_sin + (int64_t)j * half + piece * 4);
-        v[0] = rotate_pair(v[0], c.x, s.x);
-        v[1] = rotate_pair(v[1], c.y, s.y);
-        v[2] = rotate_pair(v[2], c.z, s.z);
-        v[3] = rotate_pair(v[3], c.w, s.w);
+        v[0] = rotate_pair<F16>(v[0], c.x, s.x);
+        v[1] = rotate_pair<F16>(v[1], c.y, s.y);
+        v[2] = rotate_pair<F16>(v[2], c.z, s.z);
+        v[3] = rotate_pair<F16>(v[3], c.w, s.w);
     }
     unsigned short *dst = (unsigned short *)a.out +
                           (((int64_t)b * a.seqlen_k + j) * a.heads_kv + kvh) * D + piece * 8;
@@ -60,11 +68,16 @@ __global__ __launch_bounds__(256) void rope_k_bf16_kernel(RopeKArgs a) {
 
 }  // namespace
 
-hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, hipStream_t s) {
+hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, bool f16, hipStream_t s) {
     const int keys = 256 / (head_dim / 8);
     const dim3 grid((unsigned)((a.seqlen_k + keys - 1) / keys), (unsigned)a.batch, (unsigned)a.heads_kv);
-    if (head_dim == 128) hipLaunchKernelGGL(rope_k_bf16_kernel<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(rope_k_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+    if (f16) {
+        if (head_dim == 128) hipLaunchKernelGGL((rope_k_bf16_kernel<128, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rope_k_bf16_kernel<64, true>), grid, dim3(256), 0, s, a);
+    } else {
+        if (head_dim == 128) hipLaunchKernelGGL((rope_k_bf16_kernel<128, false>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((rope_k_bf16_kernel<64, false>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

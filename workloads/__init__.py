@@ -31,6 +31,7 @@ from typing import Optional
 import numpy as np
 
 BF16_QNAN = np.uint16(0x7FC0)
+F16_QNAN = np.uint16(0x7E00)
 
 
 # --------------------------------------------------------------------------
@@ -58,15 +59,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 view of stored values (bf16 bits or fp32)."""
+    """Exact float64 view of stored values (bf16 bits, half bits or fp32)."""
     if dtype == "bf16":
         return bf16_bits_to_f32(a).astype(np.float64)
+    if dtype == "f16":
+        return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        # IEEE half by NumPy's round-to-nearest-even cast, kept as bit patterns
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
@@ -190,7 +196,7 @@ def _store_rows(rows, dtype, kv_dtype, Hkv):
     per-KV-head scales (fp8: scale = max |x| over the head's rows / 448, in
     fp32, and codes = E4M3(x / scale))."""
     if kv_dtype is None:
-        fill = BF16_QNAN if dtype == "bf16" else np.float32(np.nan)
+        fill = {"bf16": BF16_QNAN, "f16": F16_QNAN}.get(dtype, np.float32(np.nan))
         return [_store(r, dtype) for r in rows], fill, None
     if kv_dtype != "fp8_e4m3":
         raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
