@@ -15,8 +15,10 @@ After the timed steps, the same two calls are timed with ALiBi slopes
 (reported under "alibi"), and the decode call over the same logical cache
 held in a paged pool of 16-row pages in shuffled order (under "paged") and
 as FP8 E4M3 codes with per-KV-head scales (under "fp8_kv"), the prefill
-with RoPE over all 128 dims (under "rope") and with an explicit [1, 1, 1, N]
-additive mask (under "attn_mask"); none of these is part of the step.
+with RoPE over all 128 dims (under "rope"), with an explicit [1, 1, 1, N]
+additive mask (under "attn_mask"), and in IEEE half (under "f16", same draws
+rounded to half; fp16 dense MFMA peak = bf16's); none of these is part of the
+step.
 
 Printed: ONE JSON line.  ``value`` is prefill throughput in TFLOP/s on the
 algorithmic flop count (only visible (query, key) pairs: 4*d*H*N(N+1)/2);
@@ -37,7 +39,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 (and fp16) MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -253,6 +255,22 @@ def main():
     torch.cuda.synchronize()
     pre_m = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_m]))
 
+    # the same causal prefill in IEEE half (the FP16 of the BERT benchmark)
+    ph = workloads.make_prefill(3, B, N, N, H, H, d, "f16", causal=True)
+    qh, kh, vh = (torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
+                  for x in (ph.q, ph.k, ph.v))
+    oh = torch.empty_like(qh)
+    fa.prefill(qh, kh, vh, causal=True, scale=ph.scale, out=oh, lse=lse)
+    torch.cuda.synchronize()
+    ev_h = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_alibi)]
+    for e in ev_h:
+        e[0].record()
+        fa.prefill(qh, kh, vh, causal=True, scale=ph.scale, out=oh, lse=lse)
+        e[1].record()
+    torch.cuda.synchronize()
+    pre_h = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_h]))
+    del qh, kh, vh, oh
+
     # the decode over a paged pool holding the same logical cache
     page = 16
     pp = workloads.make_workload_paged(5, page)
@@ -343,6 +361,10 @@ def main():
         "rope": {"rotary_dim": d, "prefill_ms_mean": round(pre_r, 4),
                  "prefill_tflops": round(flops / (pre_r * 1e-3) / 1e12, 2),
                  "note": "K rotation pass + attention with Q rotated at load", "calls": n_alibi},
+        "f16": {"prefill_ms_mean": round(pre_h, 4),
+                "prefill_tflops": round(flops / (pre_h * 1e-3) / 1e12, 2),
+                "frac_of_f16_peak": round(flops / (pre_h * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "calls": n_alibi},
         "attn_mask": {"shape": [1, 1, 1, N], "prefill_ms_mean": round(pre_m, 4),
                       "prefill_tflops": round(flops / (pre_m * 1e-3) / 1e12, 2), "calls": n_alibi},
         "fp8_kv": {"format": "e4m3", "decode_ms_mean": round(dec_f, 4),
