@@ -158,3 +158,32 @@ def test_long_cache_many_chunks():
                                lengths=np.array([60000, 33333], dtype=np.int32))
     _case(dp, "long cache, 128-key chunks", chunk_keys=128)
     _case(dp, "long cache, library chunks")
+
+
+def test_batch_offsets_beyond_2_31_elements():
+    """Maximum sizes: caches of 64 sequences x 65536 rows x 8 KV heads x 128
+    dims (8 GiB each in bf16), so the last sequence starts 63 x 2^26 elements
+    (8 GiB) in.  Sequences 0-62 hold up to 600 seeded rows, the last one is
+    full (65536 rows, 64 partial chunks); every other row is NaN."""
+    B, cap, Hq, Hkv, d = 64, 65536, 32, 8, 128
+    short = workloads.make_decode(191, B - 1, Hq, Hkv, d, 600, (1, 600), "bf16")
+    full = workloads.make_decode(192, 1, Hq, Hkv, d, cap, (cap, cap), "bf16")
+    say(f"[decode] offsets past 2^31 elements: B={B} cap={cap} last length {int(full.seqlens_k[0])}")
+    kc, vc = (torch.full((B, cap, Hkv, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+              for _ in range(2))
+    kc[:B - 1, :600] = dev_tensor(short.k_cache, "bf16")
+    vc[:B - 1, :600] = dev_tensor(short.v_cache, "bf16")
+    kc[B - 1] = dev_tensor(full.k_cache[0], "bf16")
+    vc[B - 1] = dev_tensor(full.v_cache[0], "bf16")
+    assert kc[B - 1].data_ptr() - kc.data_ptr() == (B - 1) * cap * Hkv * d * 2
+    q = torch.cat([dev_tensor(short.q, "bf16"), dev_tensor(full.q, "bf16")])
+    sk = torch.from_numpy(np.concatenate([short.seqlens_k, full.seqlens_k])).to(DEV)
+    o, lse = fa.decode(q, kc, vc, sk, scale=short.scale)
+    torch.cuda.synchronize()
+    del kc, vc
+    torch.cuda.empty_cache()
+    o, lse = to_np(o), lse.cpu().numpy().astype(np.float64)
+    ro, rl = oracle_decode(short)
+    check(o[:B - 1], lse[:B - 1], ro, rl, "bf16", "short sequences, offsets past 2^31")
+    ro, rl = oracle_decode(full)
+    check(o[B - 1:], lse[B - 1:], ro, rl, "bf16", "full 65536-row sequence at offset 2^32+")

@@ -333,3 +333,38 @@ def test_long_sequence_sampled_rows():
     p = workloads.make_prefill(160, 1, 40000, 40000, 1, 1, 128, "bf16", causal=True)
     rows = np.array([0, 1, 255, 256, 20000, 39743, 39744, 39998, 39999])
     _sampled(p, "causal N40000 H1", rows, np.array([0]))
+
+
+def test_batch_offsets_beyond_2_31_elements():
+    """Maximum sizes: a padded extent of 3 x 131072 rows x 64 heads x 128 dims
+    (6 GiB per bf16 tensor), so the third sequence starts 2^31 elements (4 GiB)
+    into Q, K, V and O.  The valid prefixes (seeded, at most 512 rows) sit at
+    the start of each sequence and everything else is NaN; the padded query
+    rows must come back O = 0, LSE = -inf, and the valid ones match the oracle
+    on the same values."""
+    B, N, H, d = 3, 131072, 64, 128
+    p = workloads.make_prefill(190, B, 512, 512, H, H, d, "bf16", causal=True,
+                               seqlens_k_range=(100, 512), seqlens_q_equal_k=True,
+                               poison_padding=True)
+    say(f"[prefill] offsets past 2^31 elements: B={B} N={N} H={H} lengths={list(p.seqlens_k)}")
+    q, k, v = (torch.full((B, N, H, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+               for _ in range(3))
+    for big, small in zip((q, k, v), (p.q, p.k, p.v)):
+        big[:, :512] = dev_tensor(small, "bf16")
+    assert q[2].data_ptr() - q.data_ptr() == 2 ** 31 * 2
+    sl = torch.from_numpy(p.seqlens_k).to(DEV)
+    o, lse = fa.prefill(q, k, v, causal=True, scale=p.scale, seqlens_q=sl, seqlens_k=sl)
+    torch.cuda.synchronize()
+    del q, k, v
+    assert int(o[:, 512:].abs().amax()) == 0, "padded rows beyond the drawn prefix not zero"
+    assert bool(torch.all(lse[:, :, 512:] == float("-inf")))
+    heads = [0, 31, 63]
+    ro, rl = oracle_prefill(p, heads=heads)
+    check(to_np_rows(o[:, :512, heads]), lse[:, heads, :512].cpu().numpy().astype(np.float64),
+          ro, rl, "bf16", "offsets past 2^31 elements")
+    del o, lse
+    torch.cuda.empty_cache()
+
+
+def to_np_rows(t):
+    return t.float().cpu().numpy().astype(np.float64)
