@@ -315,8 +315,8 @@ def test_decode_workspace_rules(lib):
     p = _decode()
     st, n = _lib.decode_workspace_size(p)
     assert st == _lib.FA_OK
-    # library choice at this size is 1024-key chunks: 8 chunks of 64*32 rows
-    rows = 64 * 32 * 8
+    # library choice at this size is 2048-key chunks: 4 chunks of 64*32 rows
+    rows = 64 * 32 * 4
     expect = ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
     assert n == expect
     assert _lib.decode_fwd(p, None, n, 0) == _lib.FA_ERR_WORKSPACE

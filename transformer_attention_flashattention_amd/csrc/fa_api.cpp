@@ -86,12 +86,13 @@ int decode_heads_per_wg(int group) {
 
 int decode_chunk(const fa_decode_params *p, int gt) {
     if (p->chunk_keys > 0) return p->chunk_keys;
-    // Longest chunk (fewest partials to combine) that still gives about 16
-    // workgroups per CU when every sequence is at capacity; every workgroup
-    // streams its chunk with four wavefronts of 32-key tiles.
+    // Longest chunk, up to 2048 keys (fewest partials to combine, fewest
+    // pipeline fills per key), that still gives about 8 workgroups per CU
+    // when every sequence is at capacity; every workgroup streams its chunk
+    // with four wavefronts of 16- or 32-key tiles.
     const long long groups = (long long)p->batch * p->heads_kv * (p->heads_q / p->heads_kv / gt);
-    int c = 1024;
-    while (c > fa::kDecodeChunkUnit && groups * ((p->cache_capacity + c - 1) / c) < 4096) c >>= 1;
+    int c = 2048;
+    while (c > fa::kDecodeChunkUnit && groups * ((p->cache_capacity + c - 1) / c) < 2048) c >>= 1;
     return c;
 }
 
