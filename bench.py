@@ -198,6 +198,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the same prefill calls back to back, with no decode between them (outside
+    # the timed steps; reported beside them, never as the value)
+    n_b2b = max(5, args.steps // 2)
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_b[0].record()
+    for _ in range(n_b2b):
+        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
+    ev_b[1].record()
+    torch.cuda.synchronize()
+    pre_b2b = ev_b[0].elapsed_time(ev_b[1]) / n_b2b
+
     # the ALiBi variants of both calls (slopes 2^(-8(h+1)/H)), timed the same way
     def alibi_slopes(H):
         return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32,
@@ -348,6 +359,12 @@ def main():
                     "ms_median": round(float(np.median(pre_ms)), 4),
                     "ms_min": round(float(pre_ms.min()), 4),
                     "algorithmic_flop": flops},
+        "prefill_back_to_back": {"ms_mean": round(pre_b2b, 4),
+                                 "tflops": round(flops / (pre_b2b * 1e-3) / 1e12, 2),
+                                 "frac_of_bf16_peak": round(flops / (pre_b2b * 1e-3) / 1e12
+                                                            / PEAK_BF16_TFLOPS, 4),
+                                 "calls": n_b2b,
+                                 "note": "the same prefill calls with no decode between them"},
         "decode": {"value": round(gbs, 1), "unit": "GB/s",
                    "ms_mean": round(float(dec_ms.mean()), 4),
                    "ms_median": round(float(np.median(dec_ms)), 4),
