@@ -212,12 +212,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float mo[NWAVES][GT][D];    // merge: P.V
     __shared__ float mml[NWAVES][GT][2];                                 // merge: (m, l)
 
-    // Work items are the (sequence, chunk) pairs that exist, in that order,
-    // each taken by heads_kv * head_groups consecutive workgroups: KV head
-    // (group slice) varies fastest, so workgroups dispatched together read the
-    // rows of all KV heads of one key range (interleaved in the BSHD cache),
-    // and consecutive items sweep the cache in address order.  The grid is
-    // sized for every sequence at capacity; workgroups past the last item exit.
+    // Work items are the (sequence, chunk) pairs that exist, each taken by
+    // heads_kv * head_groups consecutive workgroups: KV head (group slice)
+    // varies fastest, so workgroups dispatched together read the rows of all
+    // KV heads of one key range (interleaved in the BSHD cache).  Within each
+    // block of 64 sequences the items come longest chunk first (ties by
+    // sequence index, a sequence's chunks together), so the last workgroups
+    // of the launch are its shortest and the tail, where too few workgroups
+    // remain to keep HBM busy, stays short.  The grid is sized for every
+    // sequence at capacity; workgroups past the last item exit.
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int slots = a.heads_kv * a.head_groups;
@@ -227,21 +230,25 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     const int kvh = slot / a.head_groups;
     int b = -1, chunk = 0;
     {
-        int before = 0;                            // items of sequences b0 - 1 and below
+        int before = 0;                            // items of the blocks before b0
         for (int b0 = 0; b0 < a.batch; b0 += 64) {
-            int n = 0;
+            int n = 0, len = 0;
             if (b0 + lane < a.batch) {
-                int lo_, L_, len_;
+                int lo_, L_;
                 visible_range(a, b0 + lane, lo_, L_);
-                chunking(a, lo_, L_, n, len_);
+                chunking(a, lo_, L_, n, len);
             }
-            int incl = n;                          // inclusive scan over the wavefront
+            // items ahead of this lane's: those of the sequences with longer
+            // chunks, or equal chunks and a lower index
+            int ahead = 0, total = 0;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
+            for (int k = 0; k < 64; ++k) {
+                const int len_k = __builtin_amdgcn_readlane(len, k);
+                const int n_k = __builtin_amdgcn_readlane(n, k);
+                ahead += (len_k > len || (len_k == len && k < lane)) ? n_k : 0;
+                total += n_k;
             }
-            const int excl = before + incl - n;
+            const int excl = before + ahead;
             const unsigned long long hit = __ballot(n > 0 && item >= excl && item < excl + n);
             if (hit) {
                 const int src = __ffsll((long long)hit) - 1;
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 chunk = item - __shfl(excl, src);
                 break;
             }
-            before += __shfl(incl, 63);
+            before += total;
         }
     }
     if (b < 0) return;                             // past the last work item
