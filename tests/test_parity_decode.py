@@ -38,6 +38,24 @@ def test_lengths_around_chunk_edges(chunk):
     _case(dp, f"lengths at chunk edges, chunk={chunk}", chunk_keys=chunk)
 
 
+@pytest.mark.parametrize("chunk", [0, 128, 384])
+def test_many_sequences_work_order(chunk):
+    # more than one block of 64 sequences (the split kernel orders each
+    # block's work items longest chunk first): repeated lengths (ties),
+    # empty sequences, and sequences that fill the capacity
+    rng = np.random.default_rng(70)
+    lengths = rng.integers(1, 700, size=150).astype(np.int32)
+    lengths[[3, 64, 65, 127, 128, 149]] = 0
+    lengths[[10, 20, 70, 140]] = 700
+    lengths[30:40] = 257
+    dp = workloads.make_decode(71, len(lengths), 8, 2, 128, 700, (1, 700), "bf16",
+                               lengths=lengths)
+    o, lse = _case(dp, f"150 sequences, chunk={chunk}", chunk_keys=chunk)
+    # no atomics and a fixed order: the same call again is bit-identical
+    o2, lse2 = run_decode(dp, chunk_keys=chunk)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (6, 2), (8, 1), (12, 4)])
 def test_gqa_groups(Hq, Hkv):
     dp = workloads.make_decode(51 + Hq, 5, Hq, Hkv, 128, 900, (1, 900), "bf16")
