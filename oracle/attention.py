@@ -84,7 +84,12 @@ notes):
   ``i + Lk - Lq``.  Q and K are rotated first and, as the page's separate
   form (apply_rope, then flash_attention) stores them, held in the input
   dtype: each rotated element is rounded to nearest even in bf16 (or fp32).
-  Attention over the rotated vectors is unchanged.
+  Attention over the rotated vectors is unchanged.  When a sequence has
+  more query rows than keys (Lq > Lk), the first Lq - Lk query rows sit at
+  negative positions, which the tables do not hold; the page defines no
+  rotation there.  With RoPE such a row has no visible key: O = 0 and
+  LSE = -inf.  (Under the causal mask these rows are empty anyway; the rule
+  matters only without it.)
 
 Every function here is pinned in ``tests/test_oracle.py`` against closed
 forms, brute force on tiny integer inputs, library routines and invariants.
@@ -158,6 +163,10 @@ def rope_rotate(x: np.ndarray, positions, cos_table, sin_table, rotary_dim: int,
     if rotary_dim % 2 or rotary_dim > x.shape[-1]:
         raise ValueError("rotary_dim must be even and at most the row length")
     pos = np.asarray(positions, dtype=np.int64)
+    # positions index the tables directly: one outside [0, rows) has no angle
+    # (NumPy would wrap a negative index to the end of the table)
+    if pos.size and (pos.min() < 0 or pos.max() >= len(cos_table)):
+        raise ValueError("RoPE position outside the tables")
     half = rotary_dim // 2
     c = np.asarray(cos_table, dtype=np.float32)[pos][:, :half].astype(np.float64)
     s = np.asarray(sin_table, dtype=np.float32)[pos][:, :half].astype(np.float64)
@@ -216,6 +225,8 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
     (at ``i + Lk - Lq``) and K rows (at ``j``) before the scores, rounding
     the rotated elements to ``store`` ("bf16", "f32" or None); only rows
     inside the valid lengths are rotated (the others are never visible).
+    A query row at a negative position (``i < Lq - Lk``) has no angle in the
+    tables, so under RoPE it sees no key.
     ``attn_mask`` (float array broadcastable to [B, Hq, Nq, Nk]) is added to
     the scaled scores.
     """
@@ -247,7 +258,10 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, scale: float,
         if rope is not None:
             cos_t, sin_t, rdim = rope[:3]
             store = rope[3] if len(rope) > 3 else None
-            q_ok = np.flatnonzero(rows < Lq)          # rows inside the valid length
+            # rows before position 0 have no rotation: they see nothing
+            vis[rows + (Lk - Lq) < 0] = False
+            # rows inside the valid length, at a position the tables hold
+            q_ok = np.flatnonzero((rows < Lq) & (rows + (Lk - Lq) >= 0))
             k_ok = np.arange(min(Lk, Nk))
         for hi, h in enumerate(heads):
             kvh = h // group

@@ -790,6 +790,54 @@ def test_rope_decode_query_at_last_position():
         np.testing.assert_allclose(l[b], rl[0, :, 0], rtol=0, atol=1e-13)
 
 
+def test_rope_rejects_positions_outside_the_tables():
+    cos_t, sin_t = _angle_tables(10, 4)
+    x = np.ones((2, 8))
+    with pytest.raises(ValueError):
+        oracle.rope_rotate(x, [-1, 3], cos_t, sin_t, 8)
+    with pytest.raises(ValueError):
+        oracle.rope_rotate(x, [0, 10], cos_t, sin_t, 8)
+    oracle.rope_rotate(x, [0, 9], cos_t, sin_t, 8)
+
+
+def _rotate_complex(x, pos, cos_t, sin_t, rdim):
+    """Independent coding of the pair rotation: complex multiplication."""
+    x = np.array(x, dtype=np.float64)
+    z = (x[:, 0:rdim:2] + 1j * x[:, 1:rdim:2]) * (
+        cos_t[pos, :rdim // 2].astype(np.float64) + 1j * sin_t[pos, :rdim // 2].astype(np.float64))
+    x[:, 0:rdim:2], x[:, 1:rdim:2] = z.real, z.imag
+    return x
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rope_more_queries_than_keys(causal):
+    """Lq > Lk: query row i sits at i + Lk - Lq; the first Lq - Lk rows have
+    no position in the tables and see nothing under RoPE (causal: they are
+    empty anyway).  The other rows match the scalar loop over inputs rotated
+    by complex multiplication.  Static extents (Nq 6, Nk 3) and valid lengths
+    (seqlens_k 2 and 6 of 6) both."""
+    rng = np.random.default_rng(90)
+    cos_t, sin_t = _angle_tables(8, 4)
+    rope = (cos_t, sin_t, 8)
+    for Nq, Nk, lens in ((6, 3, None), (6, 6, [2, 6])):
+        B = 1 if lens is None else 2
+        q = rng.integers(-3, 4, (B, Nq, 1, 8)).astype(np.float64)
+        k = rng.integers(-3, 4, (B, Nk, 1, 8)).astype(np.float64)
+        v = rng.integers(-3, 4, (B, Nk, 1, 8)).astype(np.float64)
+        o, l = oracle.attention(q, k, v, scale=0.25, causal=causal, rope=rope, seqlens_k=lens)
+        for b in range(B):
+            Lk = Nk if lens is None else lens[b]
+            off = Lk - Nq
+            first = max(0, -off)                      # rows before position 0
+            qr = _rotate_complex(q[b, first:, 0], np.arange(first, Nq) + off, cos_t, sin_t, 8)
+            kr = _rotate_complex(k[b, :Lk, 0], np.arange(Lk), cos_t, sin_t, 8)
+            vis = [[(not causal) or j <= i + off for j in range(Lk)] for i in range(first, Nq)]
+            so, sl = _scalar_attention(qr.tolist(), kr.tolist(), v[b, :Lk, 0].tolist(), 0.25, vis)
+            assert np.all(o[b, :first, 0] == 0.0) and np.all(l[b, 0, :first] == -np.inf)
+            np.testing.assert_allclose(o[b, first:, 0], np.array(so), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l[b, 0, first:], np.array(sl), rtol=0, atol=1e-12)
+
+
 def test_round_to_dtype_single_rounding_to_nearest_even():
     # ties go to the even neighbour; a value just above a tie goes up, which
     # rounding through fp32 first (double rounding) would get wrong
