@@ -110,9 +110,13 @@ typedef enum {
  * (x, y) -> (x c - y s, x s + y c), c = rope_cos[m * rotary_dim / 2 + p],
  * s = rope_sin[...] (device fp32 tables [rope_max_pos, rotary_dim / 2]; the
  * page gives no angle formula, so the caller supplies the tables).  Key j
- * sits at position j, query row i at i + (Lk - Lq).  The rotated vectors are
- * rounded to the input dtype before the products, as a separate rotation
- * pass would store them.  Queries are rotated in registers as they are
+ * sits at position j, query row i at i + (Lk - Lq).  When a sequence has
+ * more query rows than keys (Lq > Lk), its rows i < Lq - Lk sit before
+ * position 0, where the tables hold no angle: with RoPE those rows see no
+ * key and get O = 0, LSE = -inf (under the causal mask they are empty
+ * anyway), and no table entry outside [0, rope_max_pos) is read.  The
+ * rotated vectors are rounded to the input dtype before the products, as a
+ * separate rotation pass would store them.  Queries are rotated in registers as they are
  * loaded.  Keys: the fp32 path rotates each key tile as it is staged; the
  * bf16 path first rotates K once into `workspace` (a copy of K's valid rows,
  * contiguous [batch, seqlen_k, heads_kv, head_dim]), since its kernel reads
@@ -315,7 +319,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10600
+#define FA_ABI_VERSION 10601
 
 #ifdef __cplusplus
 }

@@ -67,6 +67,23 @@ def test_rope_prefill_fewer_queries_than_keys():
     _prefill_case(p, 128, "Nq 100 < Nk 900, MQA")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_prefill_more_queries_than_keys(causal, dtype):
+    """Lq > Lk: rows i < Lq - Lk sit before position 0 and see no key under
+    RoPE (O = 0, LSE = -inf); the tables hold exactly Nk rows, so a read at a
+    negative position would leave them.  Static extents (Nq 700 > Nk 300, the
+    rows before 400 empty) and valid key lengths below the query extent (the
+    BERT-shaped call: Nq = Nk = 512, seqlens_k in [128, 512], all query rows
+    computed)."""
+    d = 128 if dtype == "bf16" else 64
+    p = workloads.make_prefill(95, 1, 700, 300, 4, 2, d, dtype, causal=causal)
+    _prefill_case(p, d, f"Nq 700 > Nk 300 {dtype}")
+    p = workloads.make_prefill(96, 4, 512, 512, 4, 4, 64, dtype, causal=causal,
+                               seqlens_k_range=(128, 512), poison_padding=True)
+    _prefill_case(p, 64, f"seqlens_k in [128, 512] < Nq 512 {dtype}")
+
+
 def test_rope_prefill_d64_window_alibi():
     p = workloads.make_prefill(93, 2, 520, 520, 6, 3, 64, "bf16", causal=True, window_left=100)
     _prefill_case(p, 32, "d64 window 100, rotary 32")

@@ -258,8 +258,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int q0 = qtile * BM;
     const int offset = Lk - Lq;           // bottom-right causal alignment
     const int W = a.window_left;
+    // RoPE: rows before position 0 (i < Lq - Lk) have no angle in the tables
+    // and see no key; the valid rows are [q_first, Lq)
+    const int q_first = ROPE ? max(0, -offset) : 0;
 
-    // visible key range [lo, hi) of a block of rows [r0, r1] (all < Lq)
+    // visible key range [lo, hi) of a block of rows [r0, r1] (all valid)
     auto key_range = [&](int r0, int r1, int &lo, int &hi) {
         lo = 0;
         hi = Lk;
@@ -267,7 +270,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if (W > 0) lo = max(0, r0 + offset - W + 1);
     };
     int wg_lo = 0, wg_hi = 0;
-    if (q0 < Lq) key_range(q0, min(q0 + BM, Lq) - 1, wg_lo, wg_hi);
+    const int wg_r0 = ROPE ? max(q0, q_first) : q0;
+    if (wg_r0 < min(q0 + BM, Lq)) key_range(wg_r0, min(q0 + BM, Lq) - 1, wg_lo, wg_hi);
     const int t_begin = wg_lo / BN;
     const int ntiles = (wg_hi > wg_lo) ? (wg_hi + BN - 1) / BN - t_begin : 0;
 
@@ -275,9 +279,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int qi = q0w + l32;             // this lane's query row
     // tiles (relative to t_begin) this wavefront has to visit: [w_lo, w_hi)
     int w_lo = 0, w_hi = 0;
-    if (q0w < Lq && ntiles > 0) {
+    const int w_r0 = ROPE ? max(q0w, q_first) : q0w;
+    if (w_r0 < min(q0w + 32, Lq) && ntiles > 0) {
         int lo, hi;
-        key_range(q0w, min(q0w + 32, Lq) - 1, lo, hi);
+        key_range(w_r0, min(q0w + 32, Lq) - 1, lo, hi);
         if (hi > lo) {
             w_lo = lo / BN - t_begin;
             w_hi = (hi + BN - 1) / BN - t_begin;
@@ -305,7 +310,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // ---- Q fragment (B operand), zero for rows outside the valid length ---
     v8 qf[KSTEPS];
     {
-        const bool ok = qi < Lq;
+        const bool ok = qi < Lq && (!ROPE || qi >= q_first);
         const unsigned short *row = Qp + (int64_t)qi * a.q_ss + half * 8;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -314,8 +319,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
             qf[ks] = __builtin_bit_cast(v8, v);
         }
         // RoPE: the lane's 8 dims of a k-step are 4 adjacent pairs, turned by
-        // the angles of its row's position (qi + Lk - Lq); the result is
-        // rounded to bf16, the operand precision
+        // the angles of its row's position (qi + Lk - Lq >= 0 for the rows
+        // loaded); the result is rounded to bf16, the operand precision
         if constexpr (ROPE) {
             if (ok) {
                 const int rhalf = a.rotary_dim / 2;
@@ -412,7 +417,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
     const int pos = qi + offset;                     // key position of this row
     const float c2 = a.scale_log2;
-    const int vis_hi = a.causal ? min(Lk, pos + 1) : Lk;
+    const int vis_hi = (ROPE && qi < q_first) ? 0 : (a.causal ? min(Lk, pos + 1) : Lk);
     const int vis_lo = (W > 0) ? pos - W + 1 : INT_MIN;
     // ALiBi in raw score units (the accumulators hold q.k; the exponent is
     // scale_log2 * s): scale * s - m |pos - j| = scale * (s - (m / scale) |pos - j|)
@@ -524,7 +529,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const int k0 = (t_begin + tile_of(j)) * BN;
         const bool need_mask = (k0 + BN > Lk) ||
                                (a.causal && k0 + BN - 1 > q0w + offset) ||
-                               (W > 0 && k0 <= q0w + 31 + offset - W);
+                               (W > 0 && k0 <= q0w + 31 + offset - W) ||
+                               (ROPE && q0w < q_first);
         if constexpr (ALIBI) {
             // distance |pos - key| with key = k0 + half*8 + sb*32 + 16*(r/8) + r%8
             const float base = (float)(pos - k0 - half * 8);

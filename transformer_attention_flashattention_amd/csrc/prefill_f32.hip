@@ -42,16 +42,20 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
     const int q0 = qtile * BM;
     const int offset = Lk - Lq;
     const int W = a.window_left;
+    // RoPE: rows before position 0 (i < Lq - Lk) have no angle in the tables
+    // and see no key; the valid rows are [q_first, Lq)
+    const int q_first = a.rotary_dim > 0 ? max(0, -offset) : 0;
+    const int r0 = max(q0, q_first);
 
     int kv_lo = 0, kv_hi = Lk;
-    if (q0 < Lq) {
+    if (r0 < Lq) {
         const int q_last = min(q0 + BM, Lq) - 1;
         if (a.causal) kv_hi = min(kv_hi, q_last + offset + 1);
-        if (W > 0) kv_lo = max(0, q0 + offset - W + 1);
+        if (W > 0) kv_lo = max(0, r0 + offset - W + 1);
     }
     int t_begin = kv_lo / BN;
     int t_end = (kv_hi + BN - 1) / BN;
-    if (q0 >= Lq || kv_hi <= kv_lo) t_end = t_begin;
+    if (r0 >= min(q0 + BM, Lq) || kv_hi <= kv_lo) t_end = t_begin;
 
     const float *Qp = (const float *)a.q + b * a.q_sb + h * a.q_sh;
     const float *Kp = (const float *)a.k + b * a.k_sb + kvh * a.k_sh;
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
         const int r = idx / (D / 2), p = idx - (idx / (D / 2)) * (D / 2);
         const int i = q0 + r;
         float x = 0.f, y = 0.f;
-        if (i < Lq) {
+        if (i < Lq && i >= q_first) {
             x = Qp[(int64_t)i * a.q_ss + 2 * p];
             y = Qp[(int64_t)i * a.q_ss + 2 * p + 1];
             rotate(x, y, i + offset, p);
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(BM) void prefill_f32_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < BN; ++j) {
             const int key = k0 + j;
-            bool vis = key < Lk;
+            bool vis = key < Lk && qi >= q_first;
             if (a.causal) vis = vis && key <= pos;
             if (W > 0) vis = vis && key > pos - W;
             if (a.alibi) s[j] = __builtin_fmaf(fabsf((float)(pos - key)), alibi_raw, s[j]);
