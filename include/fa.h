@@ -309,6 +309,35 @@ fa_status fa_decode_workspace_size(const fa_decode_params *params, size_t *bytes
 fa_status fa_decode_fwd(const fa_decode_params *params, void *workspace,
                         size_t workspace_bytes, void *hip_stream);
 
+/*
+ * Allocation-free decode: fa_decode_fwd_noalloc
+ * ---------------------------------------------
+ * For callers that cannot allocate device memory around a decode call:
+ * code being captured into a HIP graph, tight serving loops, and harnesses
+ * that forbid allocation.  The same operation, parameters and results as
+ * fa_decode_fwd (same kernels, bit-identical output), but the partial
+ * results live in a device array of the library instead of a caller
+ * workspace: FA_DECODE_NOALLOC_MAX_BYTES per GPU, held by each GPU the
+ * library runs on from when its code is loaded there until the process
+ * ends.  The call allocates and frees nothing.  The first call on a device
+ * looks up that device's copy of the array (no allocation; make that first
+ * call outside graph capture); later calls only enqueue the two kernels on
+ * `hip_stream` (NULL = the default stream of the current device).
+ *
+ * A parameter set whose fa_decode_workspace_size() exceeds
+ * FA_DECODE_NOALLOC_MAX_BYTES returns FA_ERR_WORKSPACE without launching
+ * (use fa_decode_fwd with a workspace then).  Nothing in the array needs to
+ * start at zero: the combine kernel reads only the partials the split
+ * kernel of the same call wrote.  Every call on one GPU shares that GPU's
+ * array and overwrites what the previous call left there: calls that
+ * overlap in time on one GPU (on different streams, or from host threads
+ * without ordering) race and give wrong results; calls ordered on one
+ * stream are safe.  Returns what fa_decode_fwd returns, or FA_ERR_HIP when
+ * the array's device address cannot be found.
+ */
+#define FA_DECODE_NOALLOC_MAX_BYTES (32u << 20)
+fa_status fa_decode_fwd_noalloc(const fa_decode_params *params, void *hip_stream);
+
 /* Static string naming a status code (never NULL). */
 const char *fa_status_str(fa_status status);
 
@@ -319,7 +348,7 @@ const char *fa_last_error_message(void);
 /* ABI version of this header: major * 10000 + minor * 100 + patch. */
 int32_t fa_abi_version(void);
 
-#define FA_ABI_VERSION 10601
+#define FA_ABI_VERSION 10700
 
 #ifdef __cplusplus
 }

@@ -297,6 +297,28 @@ def test_decode_validation(lib, kw, status, needle):
         assert st2 == status
 
 
+def test_decode_noalloc_validation_before_any_hip_call(lib):
+    """fa_decode_fwd_noalloc runs the decode's argument checks, then refuses
+    a problem whose workspace would not fit its FA_DECODE_NOALLOC_MAX_BYTES
+    device array, all before touching the GPU (none of these reaches a HIP
+    call, so they run here without one)."""
+    m = re.search(r"#define FA_DECODE_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == _lib.DECODE_NOALLOC_MAX_BYTES
+    for kw, status, needle in [(dict(head_dim=80), _lib.FA_ERR_UNSUPPORTED, "head_dim"),
+                               (dict(seqlens_k=None), _lib.FA_ERR_INVALID_ARG, "seqlens_k"),
+                               (dict(window_left=0), _lib.FA_ERR_INVALID_ARG, "window")]:
+        assert _lib.decode_fwd_noalloc(_decode(**kw), 0) == status
+        assert needle in _lib.last_error()
+    # 64 x 32 heads at capacity 8192 in 128-key chunks: 8.5 MiB x 64 / 4 > 32 MiB
+    big = _decode(chunk_keys=128)
+    st, need = _lib.decode_workspace_size(big)
+    assert st == _lib.FA_OK and need > _lib.DECODE_NOALLOC_MAX_BYTES
+    assert _lib.decode_fwd_noalloc(big, 0) == _lib.FA_ERR_WORKSPACE
+    assert "fa_decode_fwd_noalloc" in _lib.last_error() and str(need) in _lib.last_error()
+    # an empty batch is a no-op
+    assert _lib.decode_fwd_noalloc(_decode(batch=0), 0) == _lib.FA_OK
+
+
 def test_decode_rejects_cache_rows_beyond_32bit_offsets(lib):
     # the split kernel addresses one sequence's rows with 32-bit byte offsets
     p = _decode(batch=1, cache_capacity=1 << 22,

@@ -23,8 +23,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import FAError  # noqa: F401
 
-__all__ = ["prefill", "prefill_workspace_size", "decode", "decode_workspace_size", "FAError",
-           "load_library"]
+__all__ = ["prefill", "prefill_workspace_size", "decode", "decode_noalloc",
+           "decode_workspace_size", "FAError", "load_library"]
 
 
 def load_library():
@@ -375,6 +375,9 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     rope = _rope(rope_cos, rope_sin, rotary_dim, dev)
     p = _decode_params(q, k_cache, v_cache, sk, out, lse if return_lse else None, scale, window,
                        chunk_keys, al, table, capacity, scales, rope)
+    if isinstance(workspace, str) and workspace == "noalloc":
+        _lib.check(_lib.decode_fwd_noalloc(p, _stream(dev)), "fa_decode_fwd_noalloc")
+        return out, (lse if return_lse else None)
     st, need = _lib.decode_workspace_size(p)
     _lib.check(st, "fa_decode_workspace_size")
     if workspace is None:
@@ -382,3 +385,16 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None, win
     ws_bytes = workspace.numel() * workspace.element_size()
     _lib.check(_lib.decode_fwd(p, workspace.data_ptr(), ws_bytes, _stream(dev)), "fa_decode_fwd")
     return out, (lse if return_lse else None)
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens_k, *, out, lse=None, **kw):
+    """``decode`` through fa_decode_fwd_noalloc: the partial results live in
+    the library's own device array, so with ``out`` (and ``lse``, or
+    ``return_lse=False``) preallocated, and device tensors for the lengths
+    (and slopes, scales, tables), the call allocates nothing.  Calls that
+    overlap in time on one GPU share that array and race; calls ordered on
+    one stream are safe.  Problems whose workspace would exceed
+    ``DECODE_NOALLOC_MAX_BYTES`` raise FAError (FA_ERR_WORKSPACE)."""
+    if kw.get("return_lse", True) and lse is None:
+        raise ValueError("decode_noalloc needs a preallocated lse (or return_lse=False)")
+    return decode(q, k_cache, v_cache, seqlens_k, out=out, lse=lse, workspace="noalloc", **kw)

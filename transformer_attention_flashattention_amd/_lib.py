@@ -28,7 +28,10 @@ FA_KV_FP8_E4M3 = 1
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_prefill_fwd", "fa_prefill_workspace_size", "fa_decode_workspace_size",
-           "fa_decode_fwd", "fa_status_str", "fa_last_error_message", "fa_abi_version")
+           "fa_decode_fwd", "fa_decode_fwd_noalloc", "fa_status_str", "fa_last_error_message",
+           "fa_abi_version")
+# bytes of the device array fa_decode_fwd_noalloc uses (FA_DECODE_NOALLOC_MAX_BYTES)
+DECODE_NOALLOC_MAX_BYTES = 32 << 20
 
 _i64x3 = ctypes.c_int64 * 3
 _i64x2 = ctypes.c_int64 * 2
@@ -140,6 +143,8 @@ def load() -> ctypes.CDLL:
     lib.fa_decode_fwd.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
     lib.fa_decode_fwd.restype = ctypes.c_int
+    lib.fa_decode_fwd_noalloc.argtypes = [ctypes.POINTER(DecodeParams), ctypes.c_void_p]
+    lib.fa_decode_fwd_noalloc.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error_message.argtypes = []
@@ -182,3 +187,7 @@ def decode_workspace_size(params: DecodeParams) -> tuple:
 def decode_fwd(params: DecodeParams, workspace: int, workspace_bytes: int, stream: int) -> int:
     return load().fa_decode_fwd(ctypes.byref(params), ctypes.c_void_p(workspace),
                                 ctypes.c_size_t(workspace_bytes), ctypes.c_void_p(stream))
+
+
+def decode_fwd_noalloc(params: DecodeParams, stream: int) -> int:
+    return load().fa_decode_fwd_noalloc(ctypes.byref(params), ctypes.c_void_p(stream))

@@ -324,19 +324,16 @@ fa_status fa_decode_workspace_size(const fa_decode_params *p, size_t *bytes) {
     return ok();
 }
 
-fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t workspace_bytes,
-                        void *hip_stream) {
-    FA_TRY(validate_decode(p));
-    FA_TRY(validate_decode_pointers(p));
-    if (p->batch == 0) return ok();
+}  // extern "C"
+
+namespace {
+
+// Limits of the launch itself (after validate_decode and
+// validate_decode_pointers, before any HIP call).
+fa_status validate_decode_launch(const fa_decode_params *p) {
     const int group = p->heads_q / p->heads_kv;
     const int gt = decode_heads_per_wg(group);
     const int chunk = decode_chunk(p, gt);
-    const size_t need = decode_ws_bytes(p, chunk);
-    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
-    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    if (workspace_bytes < need)
-        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
     const int max_chunks = (p->cache_capacity + chunk - 1) / chunk;
     // the split kernel addresses the rows of one sequence (one page when
     // paged) with 32-bit byte offsets
@@ -348,6 +345,16 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
     if ((int64_t)p->batch * p->heads_q > 0x7fffffffLL ||
         (int64_t)p->heads_kv * (group / gt) * p->batch * max_chunks > 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
+    return FA_OK;
+}
+
+// Enqueue the decode of validated parameters (batch > 0) with `workspace`
+// (device memory of at least decode_ws_bytes bytes, 16-byte aligned).
+fa_status decode_enqueue(const fa_decode_params *p, void *workspace, void *hip_stream) {
+    const int group = p->heads_q / p->heads_kv;
+    const int gt = decode_heads_per_wg(group);
+    const int chunk = decode_chunk(p, gt);
+    const int max_chunks = (p->cache_capacity + chunk - 1) / chunk;
 
     fa::DecodeArgs a{};
     a.q = p->q; a.k = p->k_cache; a.v = p->v_cache; a.o = p->o; a.lse = p->lse;
@@ -378,6 +385,48 @@ fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t works
                                                 static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode_fwd(const fa_decode_params *p, void *workspace, size_t workspace_bytes,
+                        void *hip_stream) {
+    FA_TRY(validate_decode(p));
+    FA_TRY(validate_decode_pointers(p));
+    if (p->batch == 0) return ok();
+    const size_t need = decode_ws_bytes(p, decode_chunk(p, decode_heads_per_wg(p->heads_q / p->heads_kv)));
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    FA_TRY(validate_decode_launch(p));
+    return decode_enqueue(p, workspace, hip_stream);
+}
+
+fa_status fa_decode_fwd_noalloc(const fa_decode_params *p, void *hip_stream) {
+    static_assert(FA_DECODE_NOALLOC_MAX_BYTES == fa::kDecodeScratchBytes, "scratch size");
+    FA_TRY(validate_decode(p));
+    FA_TRY(validate_decode_pointers(p));
+    if (p->batch == 0) return ok();
+    const size_t need = decode_ws_bytes(p, decode_chunk(p, decode_heads_per_wg(p->heads_q / p->heads_kv)));
+    if (need > fa::kDecodeScratchBytes)
+        return fail(FA_ERR_WORKSPACE,
+                    "this decode needs %zu bytes of scratch, more than the %zu-byte device array of "
+                    "fa_decode_fwd_noalloc; call fa_decode_fwd with a workspace instead",
+                    need, (size_t)fa::kDecodeScratchBytes);
+    FA_TRY(validate_decode_launch(p));
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "cannot find the stream's device: %s", hipGetErrorString(e));
+    void *scratch = nullptr;
+    e = fa::decode_scratch_address(dev, &scratch);
+    if (e != hipSuccess)
+        return fail(FA_ERR_HIP, "device %d: no address for the decode scratch array: %s", dev,
+                    hipGetErrorString(e));
+    return decode_enqueue(p, scratch, hip_stream);
 }
 
 }  // extern "C"

@@ -79,10 +79,16 @@ hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, bool f16, hipStr
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, int heads_per_wg, bool f16,
                               hipStream_t s);
 
+// Device address (on `device`) of the file-scope decode scratch array of
+// kDecodeScratchBytes, looked up once per device and cached.
+hipError_t decode_scratch_address(int device, void **ptr);
+
 // Tile sizes the launchers use (also needed by the host for grid sizing).
 constexpr int kPrefillBM = 256;    // query rows per workgroup (bf16 path)
 constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
 constexpr int kDecodeChunkUnit = 128;  // decode chunks: whole rounds of 4 wavefronts x 16-key tiles
 constexpr int kDecodePageUnit = 16;   // paged cache: page sizes are multiples of one tile
+// size of the allocation-free decode's scratch array (fa.h: FA_DECODE_NOALLOC_MAX_BYTES)
+constexpr size_t kDecodeScratchBytes = 32u << 20;
 
 }  // namespace fa
