@@ -45,10 +45,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
-#ifndef DECODE_NBUF
-#define DECODE_NBUF 2
-#endif
-constexpr int NBUF = DECODE_NBUF;            // tiles held in registers: 1 computing, NBUF-1 in flight
+constexpr int NBUF = 2;                      // tiles held in registers: 1 computing, 1 in flight
 constexpr float LN2 = 0.693147180559945309f;
 constexpr float RESCALE_THRESHOLD = 8.0f;    // log2 of the largest un-rescaled p
 
@@ -593,8 +590,9 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
 // One wavefront per (sequence, query head), four per workgroup.  The partial
 // P.V rows of the first 8 chunks are loaded before anything else, together
 // with every chunk's (m, l), so a sequence with at most 8 chunks (the usual
-// case: chunks are up to 1024 keys) costs one memory round trip; longer ones
-// loop over further groups of 8.  Each lane owns D / 64 dims of O.
+// case: the library picks chunks of up to 2048 keys) costs one memory round
+// trip; longer ones loop over further groups of 8.  Each lane owns D / 64
+// dims of O.
 constexpr int COMBINE_THREADS = 256;
 constexpr int COMBINE_GROUP = 8;     // partial rows loaded per round trip
 
