@@ -56,6 +56,37 @@ def test_many_sequences_work_order(chunk):
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
 
 
+def test_large_batch_item_table():
+    """Batches above 64 sequences take their work items from the table a
+    one-workgroup plan kernel writes (16 blocks of 64 per round): 1100
+    sequences (two rounds, a partial block) with empty, full and tied
+    lengths, compared on every sequence; the same call again is
+    bit-identical; a paged and an FP8 cache of 300 sequences go the same
+    way."""
+    rng = np.random.default_rng(72)
+    lengths = rng.integers(0, 300, size=1100).astype(np.int32)
+    lengths[::97] = 0
+    lengths[5::101] = 300
+    lengths[200:260] = 129
+    dp = workloads.make_decode(73, len(lengths), 4, 2, 64, 300, (0, 300), "bf16",
+                               lengths=lengths)
+    o, lse = _case(dp, "1100 sequences (item table)", chunk_keys=128)
+    o2, lse2 = run_decode(dp, chunk_keys=128)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    from gpu_helpers import oracle_decode_paged, run_decode_fp8, run_decode_paged
+    pp = workloads.make_decode_paged(74, 300, 8, 2, 128, 512, (0, 512), 32, "bf16")
+    say("[decode] 300 sequences, paged pool of 32-row pages (item table)")
+    o, lse = run_decode_paged(pp)
+    ro, rl = oracle_decode_paged(pp)
+    check(o, lse, ro, rl, "bf16", "300 sequences paged")
+    from gpu_helpers import oracle_decode_fp8
+    df = workloads.make_decode(75, 300, 8, 2, 128, 512, (0, 512), "bf16", kv_dtype="fp8_e4m3")
+    say("[decode] 300 sequences, FP8 cache (item table)")
+    o, lse = run_decode_fp8(df)
+    ro, rl = oracle_decode_fp8(df)
+    check(o, lse, ro, rl, "bf16", "300 sequences FP8")
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (6, 2), (8, 1), (12, 4)])
 def test_gqa_groups(Hq, Hkv):
     dp = workloads.make_decode(51 + Hq, 5, Hq, Hkv, 128, 900, (1, 900), "bf16")

@@ -51,6 +51,15 @@ def test_decode_noalloc_matches_workspace_call_twice():
     check(o2, l2, ro2, rl2, "bf16", "noalloc call 2")
 
 
+def test_decode_noalloc_large_batch_item_table():
+    """Above 64 sequences the work-item table also lives in the array."""
+    dp = workloads.make_decode(213, 300, 8, 2, 128, 600, (0, 600), "bf16")
+    say("[noalloc] decode B300 Hq8 Hkv2 d128 capacity 600 (item table in the array)")
+    o, lse = _both(dp)
+    ro, rl = oracle_decode(dp)
+    check(o, lse, ro, rl, "bf16", "noalloc B300")
+
+
 def test_decode_noalloc_rejects_oversize():
     """4096 sequences at capacity 1024 in 128-key chunks would need about
     136 MB of partials, beyond the array: refused on the host, before any

@@ -132,6 +132,33 @@ __device__ __forceinline__ void chunking(const DecodeArgs &a, int lo, int L, int
     len = n > 0 ? (((Lv + n - 1) / n + kDecodeChunkUnit - 1) / kDecodeChunkUnit) * kDecodeChunkUnit : 0;
 }
 
+// Work items are the (sequence, chunk) pairs that exist.  They are numbered
+// block by block, 64 sequences to a block, and within a block longest chunk
+// first (ties by sequence index, a sequence's chunks together), so the last
+// workgroups of a launch are its shortest.  For the sequences b0 + lane of
+// one block (a whole wavefront takes part): n = this lane's chunk count,
+// ahead = items of the block that come before this lane's first, total =
+// items of the block.
+__device__ __forceinline__ void rank_block(const DecodeArgs &a, int b0, int lane, int &n, int &ahead,
+                                           int &total) {
+    int len = 0;
+    n = 0;
+    if (b0 + lane < a.batch) {
+        int lo, L;
+        visible_range(a, b0 + lane, lo, L);
+        chunking(a, lo, L, n, len);
+    }
+    ahead = 0;
+    total = 0;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+        const int len_k = __builtin_amdgcn_readlane(len, k);
+        const int n_k = __builtin_amdgcn_readlane(n, k);
+        ahead += (len_k > len || (len_k == len && k < lane)) ? n_k : 0;
+        total += n_k;
+    }
+}
+
 // A buffer the launch only reads, seen through the constant address space:
 // uniform loads from it become scalar loads whose waits the compiler tracks
 // itself (through a generic pointer they become flat loads, and waiting for
@@ -209,15 +236,13 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float mo[NWAVES][GT][D];    // merge: P.V
     __shared__ float mml[NWAVES][GT][2];                                 // merge: (m, l)
 
-    // Work items are the (sequence, chunk) pairs that exist, each taken by
-    // heads_kv * head_groups consecutive workgroups: KV head (group slice)
-    // varies fastest, so workgroups dispatched together read the rows of all
-    // KV heads of one key range (interleaved in the BSHD cache).  Within each
-    // block of 64 sequences the items come longest chunk first (ties by
-    // sequence index, a sequence's chunks together), so the last workgroups
-    // of the launch are its shortest and the tail, where too few workgroups
-    // remain to keep HBM busy, stays short.  The grid is sized for every
-    // sequence at capacity; workgroups past the last item exit.
+    // Each work item (see rank_block) is taken by heads_kv * head_groups
+    // consecutive workgroups: KV head (group slice) varies fastest, so
+    // workgroups dispatched together read the rows of all KV heads of one
+    // key range (interleaved in the BSHD cache).  The grid is sized for
+    // every sequence at capacity; workgroups past the last item exit.  Up to
+    // 64 sequences (one block) each workgroup ranks the block itself; larger
+    // batches read their item from the table decode_plan_kernel wrote.
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int slots = a.heads_kv * a.head_groups;
@@ -226,34 +251,21 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     const int hg = slot % a.head_groups;
     const int kvh = slot / a.head_groups;
     int b = -1, chunk = 0;
-    {
-        int before = 0;                            // items of the blocks before b0
-        for (int b0 = 0; b0 < a.batch; b0 += 64) {
-            int n = 0, len = 0;
-            if (b0 + lane < a.batch) {
-                int lo_, L_;
-                visible_range(a, b0 + lane, lo_, L_);
-                chunking(a, lo_, L_, n, len);
-            }
-            // items ahead of this lane's: those of the sequences with longer
-            // chunks, or equal chunks and a lower index
-            int ahead = 0, total = 0;
-#pragma unroll
-            for (int k = 0; k < 64; ++k) {
-                const int len_k = __builtin_amdgcn_readlane(len, k);
-                const int n_k = __builtin_amdgcn_readlane(n, k);
-                ahead += (len_k > len || (len_k == len && k < lane)) ? n_k : 0;
-                total += n_k;
-            }
-            const int excl = before + ahead;
-            const unsigned long long hit = __ballot(n > 0 && item >= excl && item < excl + n);
-            if (hit) {
-                const int src = __ffsll((long long)hit) - 1;
-                b = b0 + src;
-                chunk = item - __shfl(excl, src);
-                break;
-            }
-            before += total;
+    if (a.ws_items) {
+        const auto *items = read_only(a.ws_items);
+        if (item < items[0]) {
+            const int e = items[1 + item];
+            b = e / a.max_chunks;
+            chunk = e - b * a.max_chunks;
+        }
+    } else {
+        int n, ahead, total;
+        rank_block(a, 0, lane, n, ahead, total);
+        const unsigned long long hit = __ballot(n > 0 && item >= ahead && item < ahead + n);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            b = src;
+            chunk = item - __shfl(ahead, src);
         }
     }
     if (b < 0) return;                             // past the last work item
@@ -587,6 +599,38 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
+// Item table of a batch of more than 64 sequences, written once per call
+// (one workgroup): items[0] = number of items, items[1 + i] = b * max_chunks
+// + chunk of item i, in the order rank_block defines.  Sixteen wavefronts
+// rank sixteen blocks at a time; a running base carries the items of the
+// blocks before them.
+constexpr int PLAN_THREADS = 1024;
+
+__global__ __launch_bounds__(PLAN_THREADS) void decode_plan_kernel(DecodeArgs a) {
+    constexpr int NW = PLAN_THREADS / 64;
+    __shared__ int block_total[NW];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int base = 0;
+    for (int r0 = 0; r0 < a.batch; r0 += NW * 64) {
+        const int b0 = r0 + wave * 64;
+        int n = 0, ahead = 0, total = 0;
+        if (b0 < a.batch) rank_block(a, b0, lane, n, ahead, total);
+        if (lane == 0) block_total[wave] = total;
+        __syncthreads();
+        int excl = base, round_total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            excl += (w < wave) ? block_total[w] : 0;
+            round_total += block_total[w];
+        }
+        for (int c = 0; c < n; ++c) a.ws_items[1 + excl + ahead + c] = (b0 + lane) * a.max_chunks + c;
+        base += round_total;
+        __syncthreads();                           // block_total is rewritten next round
+    }
+    if (threadIdx.x == 0) a.ws_items[0] = base;
+}
+
 // One wavefront per (sequence, query head), four per workgroup.  The partial
 // P.V rows of the first 8 chunks are loaded before anything else, together
 // with every chunk's (m, l), so a sequence with at most 8 chunks (the usual
@@ -689,6 +733,10 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s) {
 template <int D, bool F16>
 hipError_t launch_all(const DecodeArgs &a, int gt, hipStream_t s) {
     hipError_t e;
+    if (a.ws_items) {
+        hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     switch (gt) {
         case 1: e = launch_split<D, F16, 1>(a, s); break;
         case 2: e = launch_split<D, F16, 2>(a, s); break;

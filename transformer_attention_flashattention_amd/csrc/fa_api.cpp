@@ -172,13 +172,26 @@ fa_status validate_decode_pointers(const fa_decode_params *p) {
     return FA_OK;
 }
 
-size_t decode_ws_bytes(const fa_decode_params *p, int chunk) {
+// Decode workspace: partial O [batch, heads_q, max_chunks, head_dim] fp32
+// (256-byte aligned), then (m, l) pairs [batch, heads_q, max_chunks, 2] fp32,
+// then, for batches above kDecodeRankBatch, the item table (int32, count
+// first, then up to batch * max_chunks entries).
+struct DecodeWsLayout {
+    size_t o_bytes, ml_bytes, items_bytes;
+    size_t total() const { return o_bytes + ml_bytes + items_bytes; }
+};
+
+DecodeWsLayout decode_ws_layout(const fa_decode_params *p, int chunk) {
     const size_t max_chunks = (size_t)(p->cache_capacity + chunk - 1) / chunk;
     const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
-    const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
-    const size_t ml_bytes = rows * 2 * sizeof(float);
-    return o_bytes + ml_bytes;
+    DecodeWsLayout w;
+    w.o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
+    w.ml_bytes = (rows * 2 * sizeof(float) + 15) & ~(size_t)15;
+    w.items_bytes = p->batch > fa::kDecodeRankBatch ? (1 + (size_t)p->batch * max_chunks) * sizeof(int32_t) : 0;
+    return w;
 }
+
+size_t decode_ws_bytes(const fa_decode_params *p, int chunk) { return decode_ws_layout(p, chunk).total(); }
 
 // Workspace of a prefill call: the rotated copy of K (bf16 with RoPE only).
 size_t prefill_ws_bytes(const fa_prefill_params *p) {
@@ -376,10 +389,12 @@ fa_status decode_enqueue(const fa_decode_params *p, void *workspace, void *hip_s
     if (p->rotary_dim > 0) {
         a.rope_cos = p->rope_cos; a.rope_sin = p->rope_sin; a.rotary_dim = p->rotary_dim;
     }
-    const size_t rows = (size_t)p->batch * p->heads_q * max_chunks;
-    const size_t o_bytes = (rows * p->head_dim * sizeof(float) + 255) & ~(size_t)255;
+    const DecodeWsLayout w = decode_ws_layout(p, chunk);
     a.ws_o = static_cast<float *>(workspace);
-    a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + w.o_bytes);
+    a.ws_items = w.items_bytes ? reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + w.o_bytes +
+                                                             w.ml_bytes)
+                               : nullptr;
 
     const hipError_t e = fa::launch_decode_bf16(a, p->head_dim, gt, p->dtype == FA_DTYPE_F16,
                                                 static_cast<hipStream_t>(hip_stream));

@@ -59,6 +59,7 @@ struct DecodeArgs {
     float scale_log2;
     float *ws_o;                   // [batch, heads_q, max_chunks, head_dim] fp32
     float *ws_ml;                  // [batch, heads_q, max_chunks, 2] fp32 (m, l)
+    int32_t *ws_items;             // batch > kDecodeRankBatch: item table [1 + batch * max_chunks], else null
     const float *alibi;            // ALiBi slopes [heads_q] or null
     float scale;                   // softmax_scale
     const int32_t *block_table;    // paged cache: [batch, pages_per_seq], or null (contiguous)
@@ -88,6 +89,7 @@ constexpr int kPrefillBM = 256;    // query rows per workgroup (bf16 path)
 constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
 constexpr int kDecodeChunkUnit = 128;  // decode chunks: whole rounds of 4 wavefronts x 16-key tiles
 constexpr int kDecodePageUnit = 16;   // paged cache: page sizes are multiples of one tile
+constexpr int kDecodeRankBatch = 64;  // decode batches up to this rank their items in the split kernel
 // size of the allocation-free decode's scratch array (fa.h: FA_DECODE_NOALLOC_MAX_BYTES)
 constexpr size_t kDecodeScratchBytes = 32u << 20;
 
