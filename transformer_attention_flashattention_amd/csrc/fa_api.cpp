@@ -231,9 +231,12 @@ fa_status validate_prefill(const fa_prefill_params *p) {
         if (p->mask_stride[3] != 1) return fail(FA_ERR_UNSUPPORTED, "mask_stride[3] must be 1");
         FA_TRY(check_strides("mask", p->mask_stride, 3, vec));
     }
-    // the K rotation pass puts batch and KV head on the second and third grid axes
-    if (p->rotary_dim > 0 && half_width && (p->batch > 65535 || p->heads_kv > 65535))
-        return fail(FA_ERR_UNSUPPORTED, "RoPE with bf16 / f16 supports batch and heads_kv up to 65535");
+    // the K rotation pass puts the batch on the second grid axis and a
+    // sequence's 16-byte pieces (1024 per workgroup) on the first
+    if (p->rotary_dim > 0 && half_width &&
+        (p->batch > 65535 || (int64_t)p->seqlen_k * p->heads_kv * (p->head_dim / 8) > (1LL << 34)))
+        return fail(FA_ERR_UNSUPPORTED,
+                    "RoPE with bf16 / f16 supports a batch up to 65535 and seqlen_k x heads_kv x head_dim up to 2^37");
     return FA_OK;
 }
 
@@ -303,7 +306,12 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
     a.mask = p->attn_mask;
     a.m_sb = p->mask_stride[0]; a.m_sh = p->mask_stride[1]; a.m_ss = p->mask_stride[2];
     const bool f16 = p->dtype == FA_DTYPE_F16;
-    const int bm = p->dtype != FA_DTYPE_F32 ? fa::kPrefillBM : fa::kPrefillF32BM;
+    // bf16 at d = 128: the query heads of a GQA group share a workgroup, up to
+    // the 8 wavefronts of 32 rows (gcd(group, 8) heads of 256 / gcd positions)
+    a.gqa_pack = 1;
+    if (p->dtype == FA_DTYPE_BF16 && p->head_dim == 128)
+        while (a.gqa_pack < 8 && a.group % (2 * a.gqa_pack) == 0) a.gqa_pack *= 2;
+    const int bm = p->dtype != FA_DTYPE_F32 ? fa::kPrefillBM / a.gqa_pack : fa::kPrefillF32BM;
     a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
     if ((int64_t)a.num_q_tiles * a.heads_q * a.batch > 0x7fffffffLL)
         return fail(FA_ERR_UNSUPPORTED, "grid too large");

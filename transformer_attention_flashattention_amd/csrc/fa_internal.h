@@ -23,7 +23,8 @@ struct PrefillArgs {
     int32_t causal, window_left;
     float scale_log2;              // softmax_scale * log2(e)
     float scale;                   // softmax_scale
-    int32_t num_q_tiles;
+    int32_t num_q_tiles;           // position blocks per sequence (16-bit path: of 256 / gqa_pack)
+    int32_t gqa_pack;              // 16-bit path: query heads of one KV head per workgroup
     const float *alibi;            // ALiBi slopes [heads_q] or null
     const float *rope_cos, *rope_sin;  // RoPE tables [max_pos, rotary_dim / 2], or null
     int32_t rotary_dim;            // 0 = no RoPE

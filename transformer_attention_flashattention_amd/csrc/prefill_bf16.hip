@@ -13,14 +13,18 @@
 // exp, block-local maxima corrected to one common maximum, fp32 for max,
 // exp and normalisation while the matrix products run in 16-bit).
 //
-// Work decomposition: one workgroup = 8 wavefronts = 256 query rows of one
-// (batch, head), 32 rows per wavefront.
-//   * grid = query tiles x heads x batch; heads and batches are independent
-//     work items spread over all CUs (jsqmd.com page, section 二 "multi-head
-//     parallel strategy").  Consecutive workgroup ids differ in (batch, head)
-//     first, so the dispatcher's round-robin over the 8 XCDs keeps each head's
-//     K/V inside one XCD's L2; under a causal mask the longest query tiles are
-//     dispatched first.
+// Work decomposition: one workgroup = 8 wavefronts of 32 query rows each,
+// over one (batch, KV head): 256 / GP positions of GP query heads that share
+// that KV head (GP = gcd(heads_q / heads_kv, 8): 1 for MHA), so every K/V
+// tile in LDS serves GP heads and, under a window, the workgroup's key span
+// covers fewer positions.  Wavefront w takes head w % GP and positions
+// 32 (w / GP) .. + 31 of the workgroup's.
+//   * grid = query tiles x (batch, KV head, head slice); heads and batches
+//     are independent work items spread over all CUs (jsqmd.com page, section
+//     二 "multi-head parallel strategy").  Consecutive workgroup ids differ in
+//     (batch, KV head) first, so the dispatcher's round-robin over the 8 XCDs
+//     keeps each KV head's K/V inside one XCD's L2; under a causal mask the
+//     longest query tiles are dispatched first.
 //   * KV tiles of 64 keys move HBM -> LDS with direct-to-LDS loads
 //     (global_load_lds_dwordx4: no VGPR staging) into two K and two V buffers
 //     shared by all 8 wavefronts: the next tiles stream in while the current
@@ -219,8 +223,9 @@ __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
 // D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores;
 // ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated);
 // MASK: add an explicit additive mask read from memory; F16: the inputs are
-// IEEE half instead of bf16.
-template <int D, bool ALIBI, bool ROPE, bool MASK, bool F16>
+// IEEE half instead of bf16; PACK: a.gqa_pack query heads share the
+// workgroup (without it one head, and the work-item arithmetic is constant).
+template <int D, bool ALIBI, bool ROPE, bool MASK, bool F16, bool PACK>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
@@ -244,18 +249,33 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int l32 = lane & 31;
 
     // ---- work item --------------------------------------------------------
-    const int bh_count = a.batch * a.heads_q;
-    const int rank = blockIdx.x / bh_count;
-    const int bh = blockIdx.x - rank * bh_count;
-    const int b = bh / a.heads_q;
-    const int h = bh - b * a.heads_q;
+    const int GP = PACK ? a.gqa_pack : 1;             // query heads per workgroup
+    int rank, b, h, kvh;
+    if constexpr (PACK) {
+        const int slices = a.group / GP;              // workgroups per (position block, KV head)
+        const int units = a.batch * a.heads_kv * slices;
+        rank = blockIdx.x / units;
+        const int unit = blockIdx.x - rank * units;
+        b = unit / (a.heads_kv * slices);
+        const int kvh_slice = unit - b * (a.heads_kv * slices);
+        kvh = kvh_slice / slices;
+        // this wavefront's query head (uniform across it)
+        h = __builtin_amdgcn_readfirstlane(kvh * a.group + (kvh_slice - kvh * slices) * GP + wave % GP);
+    } else {
+        const int bh_count = a.batch * a.heads_q;
+        rank = blockIdx.x / bh_count;
+        const int bh = blockIdx.x - rank * bh_count;
+        b = bh / a.heads_q;
+        h = bh - b * a.heads_q;
+        kvh = h / a.group;
+    }
     const int qtile = a.causal ? (a.num_q_tiles - 1 - rank) : rank;
-    const int kvh = h / a.group;
 
     int Lq = a.seqlen_q, Lk = a.seqlen_k;
     if (a.seqlens_q) Lq = min(max(a.seqlens_q[b], 0), a.seqlen_q);
     if (a.seqlens_k) Lk = min(max(a.seqlens_k[b], 0), a.seqlen_k);
-    const int q0 = qtile * BM;
+    const int wg_rows = PACK ? BM / GP : BM;   // positions per workgroup
+    const int q0 = qtile * wg_rows;
     const int offset = Lk - Lq;           // bottom-right causal alignment
     const int W = a.window_left;
     // RoPE: rows before position 0 (i < Lq - Lk) have no angle in the tables
@@ -271,11 +291,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
     };
     int wg_lo = 0, wg_hi = 0;
     const int wg_r0 = ROPE ? max(q0, q_first) : q0;
-    if (wg_r0 < min(q0 + BM, Lq)) key_range(wg_r0, min(q0 + BM, Lq) - 1, wg_lo, wg_hi);
+    if (wg_r0 < min(q0 + wg_rows, Lq)) key_range(wg_r0, min(q0 + wg_rows, Lq) - 1, wg_lo, wg_hi);
     const int t_begin = wg_lo / BN;
     const int ntiles = (wg_hi > wg_lo) ? (wg_hi + BN - 1) / BN - t_begin : 0;
 
-    const int q0w = q0 + wave * 32;       // first query row of this wavefront
+    const int q0w = q0 + (PACK ? wave / GP : wave) * 32;   // first query row of this wavefront
     const int qi = q0w + l32;             // this lane's query row
     // tiles (relative to t_begin) this wavefront has to visit: [w_lo, w_hi)
     int w_lo = 0, w_hi = 0;
@@ -676,8 +696,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
 template <int D, bool F16, bool ALIBI, bool ROPE>
 void launch_mask(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-    if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16>), grid, block, 0, s, a);
+    // GQA packing is built for the bf16 d = 128 kernels; elsewhere one head
+    // per workgroup (valid for any group)
+    constexpr bool CAN_PACK = D == 128 && !F16;
+    if (a.gqa_pack > 1 && CAN_PACK) {
+        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, CAN_PACK>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, CAN_PACK>), grid, block, 0, s, a);
+    } else {
+        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, false>), grid, block, 0, s, a);
+    }
 }
 
 template <int D, bool F16, bool ALIBI>
@@ -695,7 +723,7 @@ void launch_alibi(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, bool f16, hipStream_t s) {
-    const dim3 grid((unsigned)a.num_q_tiles * a.heads_q * a.batch);
+    const dim3 grid((unsigned)a.num_q_tiles * a.heads_q / a.gqa_pack * a.batch);
     const dim3 block(NTHREADS);
     if (f16) {
         if (head_dim == 128) launch_alibi<128, true>(a, grid, block, s);
