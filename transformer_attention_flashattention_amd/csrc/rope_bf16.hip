@@ -10,9 +10,8 @@
 // wavefronts that feed the matrix core.  Instead this pass rotates each key
 // row once (key j at position j) into a contiguous copy that the attention
 // kernel then reads; queries are rotated inside the attention kernel as they
-// are loaded.  The pass streams K once: one thread per 16-byte piece (8 dims,
-// 4 pairs) of a row; a workgroup covers 256 / (D / 8) consecutive keys of one
-// (batch, KV head), so no index needs a division.
+// are loaded.  The pass streams K once, one thread per 16-byte piece (8 dims,
+// 4 pairs) at a time.
 // Rows at or beyond a sequence's valid key length are neither read nor
 // written (the attention kernel never reads them either).
 #include "fa_internal.h"
@@ -40,43 +39,59 @@ __device__ __forceinline__ unsigned rotate_pair(unsigned xy, float c, float s) {
     return __builtin_bit_cast(unsigned, r);
 }
 
+// Threads walk the rotated copy in its memory order: 16-byte pieces of whole
+// key rows across all KV heads of a sequence (piece fastest, then head, then
+// key), PER_THREAD pieces per thread spaced a workgroup apart, so loads and
+// stores cover contiguous runs of rows in the BSHD layout and the heads of a
+// row share their cos / sin entries in the caches.
+constexpr int ROPE_THREADS = 256;
+constexpr int ROPE_PER_THREAD = 4;
+
 template <int D, bool F16>
-__global__ __launch_bounds__(256) void rope_k_bf16_kernel(RopeKArgs a) {
-    constexpr int PIECES = D / 8;                        // 16-byte pieces per row
-    constexpr int KEYS = 256 / PIECES;                   // key rows per workgroup
-    const int piece = threadIdx.x % PIECES;
-    const int j = blockIdx.x * KEYS + threadIdx.x / PIECES;
-    const int b = blockIdx.y, kvh = blockIdx.z;
+__global__ __launch_bounds__(ROPE_THREADS) void rope_k_bf16_kernel(RopeKArgs a) {
+    constexpr int PIECES = D / 8;                        // 16-byte pieces per head row
+    const int b = blockIdx.y;
     const int Lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.seqlen_k) : a.seqlen_k;
-    if (j >= Lk) return;
-    const unsigned short *src =
-        (const unsigned short *)a.k + b * a.k_sb + (int64_t)j * a.k_ss + kvh * a.k_sh + piece * 8;
-    u32x4 v = *(const u32x4 *)src;
-    if (piece * 8 < a.rotary_dim) {                      // rotary_dim is a multiple of 8
-        const int half = a.rotary_dim / 2;
-        const float4 c = *(const float4 *)(a.rope_cos + (int64_t)j * half + piece * 4);
-        const float4 s = *(const float4 *)(a.rope_sin + (int64_t)j * half + piece * 4);
-        v[0] = rotate_pair<F16>(v[0], c.x, s.x);
-        v[1] = rotate_pair<F16>(v[1], c.y, s.y);
-        v[2] = rotate_pair<F16>(v[2], c.z, s.z);
-        v[3] = rotate_pair<F16>(v[3], c.w, s.w);
+    const int64_t row_pieces = (int64_t)a.heads_kv * PIECES;
+    const int64_t n_end = (int64_t)Lk * row_pieces;      // pieces of the valid rows
+    const int half = a.rotary_dim / 2;
+    const int64_t n0 = (int64_t)blockIdx.x * ROPE_THREADS * ROPE_PER_THREAD + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < ROPE_PER_THREAD; ++u) {
+        const int64_t n = n0 + (int64_t)u * ROPE_THREADS;
+        if (n >= n_end) break;
+        const int piece = (int)(n % PIECES);
+        const int64_t r = n / PIECES;
+        const int kvh = (int)(r % a.heads_kv);
+        const int j = (int)(r / a.heads_kv);
+        const unsigned short *src =
+            (const unsigned short *)a.k + b * a.k_sb + (int64_t)j * a.k_ss + kvh * a.k_sh + piece * 8;
+        u32x4 v = *(const u32x4 *)src;
+        if (piece * 8 < a.rotary_dim) {                  // rotary_dim is a multiple of 8
+            const float4 c = *(const float4 *)(a.rope_cos + (int64_t)j * half + piece * 4);
+            const float4 sn = *(const float4 *)(a.rope_sin + (int64_t)j * half + piece * 4);
+            v[0] = rotate_pair<F16>(v[0], c.x, sn.x);
+            v[1] = rotate_pair<F16>(v[1], c.y, sn.y);
+            v[2] = rotate_pair<F16>(v[2], c.z, sn.z);
+            v[3] = rotate_pair<F16>(v[3], c.w, sn.w);
+        }
+        unsigned short *dst = (unsigned short *)a.out + ((int64_t)b * a.seqlen_k * a.heads_kv + r) * D + piece * 8;
+        *(u32x4 *)dst = v;
     }
-    unsigned short *dst = (unsigned short *)a.out +
-                          (((int64_t)b * a.seqlen_k + j) * a.heads_kv + kvh) * D + piece * 8;
-    *(u32x4 *)dst = v;
 }
 
 }  // namespace
 
 hipError_t launch_rope_k_bf16(const RopeKArgs &a, int head_dim, bool f16, hipStream_t s) {
-    const int keys = 256 / (head_dim / 8);
-    const dim3 grid((unsigned)((a.seqlen_k + keys - 1) / keys), (unsigned)a.batch, (unsigned)a.heads_kv);
+    const int64_t pieces = (int64_t)a.seqlen_k * a.heads_kv * (head_dim / 8);
+    const int64_t per_wg = (int64_t)ROPE_THREADS * ROPE_PER_THREAD;
+    const dim3 grid((unsigned)((pieces + per_wg - 1) / per_wg), (unsigned)a.batch);
     if (f16) {
-        if (head_dim == 128) hipLaunchKernelGGL((rope_k_bf16_kernel<128, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((rope_k_bf16_kernel<64, true>), grid, dim3(256), 0, s, a);
+        if (head_dim == 128) hipLaunchKernelGGL((rope_k_bf16_kernel<128, true>), grid, dim3(ROPE_THREADS), 0, s, a);
+        else hipLaunchKernelGGL((rope_k_bf16_kernel<64, true>), grid, dim3(ROPE_THREADS), 0, s, a);
     } else {
-        if (head_dim == 128) hipLaunchKernelGGL((rope_k_bf16_kernel<128, false>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((rope_k_bf16_kernel<64, false>), grid, dim3(256), 0, s, a);
+        if (head_dim == 128) hipLaunchKernelGGL((rope_k_bf16_kernel<128, false>), grid, dim3(ROPE_THREADS), 0, s, a);
+        else hipLaunchKernelGGL((rope_k_bf16_kernel<64, false>), grid, dim3(ROPE_THREADS), 0, s, a);
     }
     return hipGetLastError();
 }
