@@ -14,7 +14,11 @@ library), so the per-call figures are kernel time plus launch gaps.
 Outside the timed steps, each of the five workloads gets its own entry under
 "configs": the tiny fp32 case, the BERT-shaped varlen encoder and the GQA
 window prefill are timed on their own (warm-up calls, then one event pair per
-call), and the two step workloads reuse the step's per-call events.  Each
+call), and the two step workloads reuse the step's per-call events.  These
+measurements and the variants below run first; the warm-up and timed steps
+run after them, so the steps start on a GPU that has been busy rather than
+one ramping up from idle after input generation (its first few hundred
+microseconds of work otherwise run measurably slower).  Each
 entry carries its throughput, its roofline fraction and the fp64 oracle timed
 on the host's cores on the same inputs (the whole workload, or a stated
 sample of its heads).  Further variants of the two step calls are timed the
@@ -297,32 +301,7 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    n_var = max(5, args.steps // 4)
-
-    # the same prefill calls back to back, with no decode between them (outside
-    # the timed steps; reported beside them, never as the value)
-    n_b2b = max(5, args.steps // 2)
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev_b[0].record()
-    for _ in range(n_b2b):
-        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
-    ev_b[1].record()
-    torch.cuda.synchronize()
-    pre_b2b = ev_b[0].elapsed_time(ev_b[1]) / n_b2b
-
+    n_var = 20                                  # calls per variant timing
     # ---- the other three workloads, each timed on its own -------------------
     # tiny fp32 single head, B1 H1 N128 d64, non-causal
     p1 = workloads.make_workload(1)
@@ -426,6 +405,32 @@ def main():
                                                 k_scale=ks8, v_scale=vs8), n_var, 1)
     fp8_bytes = decode_bytes(dp.seqlens_k, Hq, Hkv, dd, kv_elt=1) + 2 * 4 * Hkv
     del k8, v8
+
+    # ---- the timed steps: last, on a GPU the measurements above kept busy --
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+
+    # the same prefill calls back to back, with no decode between them (outside
+    # the timed steps; reported beside them, never as the value)
+    n_b2b = max(5, args.steps // 2)
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev_b[0].record()
+    for _ in range(n_b2b):
+        fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
+    ev_b[1].record()
+    torch.cuda.synchronize()
+    pre_b2b = ev_b[0].elapsed_time(ev_b[1]) / n_b2b
 
     # ---- figures ---------------------------------------------------------------
     flops = prefill_flops(B, H, N, d)
