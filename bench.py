@@ -446,14 +446,16 @@ def main():
         "config1": {"workload": "B1 H1 N128 d64 fp32, not causal", **ms_stats(ms1),
                     "algorithmic_flop": fl1, "algorithmic_bytes": by1,
                     "tflops": round(tf(fl1, ms1.mean()), 4),
-                    "roofline": roofline("alu", tf(fl1, ms1.mean()), PEAK_F32_TFLOPS, "TFLOP/s"),
+                    "roofline": roofline("alu", tf(fl1, ms1.mean()), PEAK_F32_TFLOPS, "TFLOP/s",
+                                         measured_traffic(["prefill_f32_kernel<64>"])),
                     "note": "one wavefront per 64 rows (2 workgroups): latency-bound; "
                             "fp32 vector peak"},
         "config2": {"workload": "B8 H12 N512 d64 bf16, key lengths U[128,512] "
                                 f"(sum {int(np.sum(p2.seqlens_k))}), all query rows",
                     **ms_stats(ms2), "algorithmic_flop": fl2, "algorithmic_bytes": by2,
                     "tflops": round(tf(fl2, ms2.mean()), 2),
-                    "roofline": roofline("mfma", tf(fl2, ms2.mean()), PEAK_BF16_TFLOPS, "TFLOP/s"),
+                    "roofline": roofline("mfma", tf(fl2, ms2.mean()), PEAK_BF16_TFLOPS, "TFLOP/s",
+                                         measured_traffic(["prefill_bf16_kernel<64, false, false, false, false, false>"])),
                     "roofline_hbm": roofline("hbm", by2 / (ms2.mean() * 1e-3) / 1e9, PEAK_HBM_GBS,
                                              "GB/s")},
         "config3": {"workload": "B1 H32 N8192 d128 bf16 causal (the step's prefill)",
@@ -464,7 +466,8 @@ def main():
         "config4": {"workload": "B2 Hq32 Hkv8 N4096 d128 bf16 causal, window 1024",
                     **ms_stats(ms4), "algorithmic_flop": fl4, "algorithmic_bytes": by4,
                     "tflops": round(tf(fl4, ms4.mean()), 2),
-                    "roofline": roofline("mfma", tf(fl4, ms4.mean()), PEAK_BF16_TFLOPS, "TFLOP/s")},
+                    "roofline": roofline("mfma", tf(fl4, ms4.mean()), PEAK_BF16_TFLOPS, "TFLOP/s",
+                                         measured_traffic(["prefill_bf16_kernel<128, false, false, false, false, true>"]))},
         "config5": {"workload": "decode B64 Hq32 Hkv8 d128 bf16, KV lengths U[512,8192] "
                                 f"(sum {int(np.sum(dp.seqlens_k))}) (the step's decode)",
                     **ms_stats(dec_ms), "algorithmic_bytes": dbytes, "gbs": round(gbs, 1),
@@ -666,23 +669,20 @@ def summarize_profiles(out):
                      "sources": srcs, "sources_sha256": sha(srcs)}
     pf = [CSRC + "prefill_bf16.hip", CSRC + "fa_internal.h"]
     dc = [CSRC + "decode_bf16.hip", CSRC + "fa_internal.h", CSRC + "fa_api.cpp"]
-    main_names = {"prefill_bf16_kernel<128>": None, "decode_split_kernel": None,
-                  "decode_combine_kernel<128>": None}
-    for kname in fetch:
-        if kname.startswith("prefill_bf16_kernel<128, false, false, false, false"):
-            main_names["prefill_bf16_kernel<128>"] = kname
-        elif kname.startswith("decode_split_kernel<128, 4, false, false, false, 16, false"):
-            main_names["decode_split_kernel"] = kname
-        elif kname.startswith("decode_combine_kernel<128, false"):
-            main_names["decode_combine_kernel<128>"] = kname
+    # the step's kernels under short keys (exact template names of the trace)
+    main_names = {"prefill_bf16_kernel<128>": "prefill_bf16_kernel<128, false, false, false, false, false>",
+                  "decode_split_kernel": "decode_split_kernel<128, 4, false, false, false, 16, false>",
+                  "decode_combine_kernel<128>": "decode_combine_kernel<128, false>"}
     for key, kname in main_names.items():
-        if kname:
+        if kname in fetch:
             ent(key, kname, pf if key.startswith("prefill") else dc)
     for kname in fetch:
         if kname in main_names.values():
             continue
         if kname.startswith("prefill_bf16"):
             ent(kname, kname, pf)
+        elif kname.startswith("prefill_f32"):
+            ent(kname, kname, [CSRC + "prefill_f32.hip", CSRC + "fa_internal.h"])
         elif kname.startswith("decode"):
             ent(kname, kname, dc)
         elif kname.startswith("rope"):
