@@ -87,7 +87,7 @@ hipError_t decode_scratch_address(int device, void **ptr);
 
 // Tile sizes the launchers use (also needed by the host for grid sizing).
 constexpr int kPrefillBM = 256;    // query rows per workgroup (bf16 path)
-constexpr int kPrefillF32BM = 64;  // query rows per workgroup (fp32 path)
+constexpr int kPrefillF32BM = 16;  // query rows per workgroup (fp32 path)
 constexpr int kDecodeChunkUnit = 128;  // decode chunks: whole rounds of 4 wavefronts x 16-key tiles
 constexpr int kDecodePageUnit = 16;   // paged cache: page sizes are multiples of one tile
 constexpr int kDecodeRankBatch = 64;  // decode batches up to this rank their items in the split kernel
