@@ -444,8 +444,8 @@ def main():
                     "tflops": round(tf(fl1, ms1.mean()), 4),
                     "roofline": roofline("alu", tf(fl1, ms1.mean()), PEAK_F32_TFLOPS, "TFLOP/s",
                                          measured_traffic(["prefill_f32_kernel<64>"])),
-                    "note": "one wavefront per 64 rows (2 workgroups): latency-bound; "
-                            "fp32 vector peak"},
+                    "note": "4 lanes per query row, 16 rows per workgroup (8 workgroups): "
+                            "latency-bound; fp32 vector peak"},
         "config2": {"workload": "B8 H12 N512 d64 bf16, key lengths U[128,512] "
                                 f"(sum {int(np.sum(p2.seqlens_k))}), all query rows",
                     **ms_stats(ms2), "algorithmic_flop": fl2, "algorithmic_bytes": by2,
