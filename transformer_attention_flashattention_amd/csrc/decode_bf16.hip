@@ -109,9 +109,12 @@ __device__ __forceinline__ float across_groups_sum(float x) {
 }
 
 // Keys [lo, L) of sequence b are visible to its decode query.
+__device__ __forceinline__ int visible_lo(const DecodeArgs &a, int L) {
+    return (a.window_left > 0) ? max(0, L - a.window_left) : 0;
+}
 __device__ __forceinline__ void visible_range(const DecodeArgs &a, int b, int &lo, int &L) {
     L = min(max(a.seqlens_k[b], 0), a.capacity);
-    lo = (a.window_left > 0) ? max(0, L - a.window_left) : 0;
+    lo = visible_lo(a, L);
 }
 
 // First key of the chunk grid: lo rounded down to a multiple of a.origin_align (1 for a
@@ -138,23 +141,28 @@ __device__ __forceinline__ void chunking(const DecodeArgs &a, int lo, int L, int
 // workgroups of a launch are its shortest.  For the sequences b0 + lane of
 // one block (a whole wavefront takes part): n = this lane's chunk count,
 // ahead = items of the block that come before this lane's first, total =
-// items of the block.
+// items of the block, L = this lane's valid length.
 __device__ __forceinline__ void rank_block(const DecodeArgs &a, int b0, int lane, int &n, int &ahead,
-                                           int &total) {
+                                           int &total, int &L) {
     int len = 0;
     n = 0;
+    L = 0;
     if (b0 + lane < a.batch) {
-        int lo, L;
+        int lo;
         visible_range(a, b0 + lane, lo, L);
         chunking(a, lo, L, n, len);
     }
+    // One key orders the lanes: chunk lengths are multiples of 128, so len / 2
+    // is a multiple of 64 and the lane term (63 - lane) only breaks ties.
+    static_assert(kDecodeChunkUnit % 128 == 0, "the order key needs len / 2 to be a multiple of 64");
+    const int key = (len >> 1) + (63 - lane);
     ahead = 0;
     total = 0;
 #pragma unroll
     for (int k = 0; k < 64; ++k) {
-        const int len_k = __builtin_amdgcn_readlane(len, k);
+        const int key_k = __builtin_amdgcn_readlane(key, k);
         const int n_k = __builtin_amdgcn_readlane(n, k);
-        ahead += (len_k > len || (len_k == len && k < lane)) ? n_k : 0;
+        ahead += key_k > key ? n_k : 0;
         total += n_k;
     }
 }
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     const int slot = blockIdx.x - item * slots;
     const int hg = slot % a.head_groups;
     const int kvh = slot / a.head_groups;
-    int b = -1, chunk = 0;
+    int b = -1, chunk = 0, L = 0;
     if (a.ws_items) {
         const auto *items = read_only(a.ws_items);
         if (item < items[0]) {
@@ -258,21 +266,21 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             b = e / a.max_chunks;
             chunk = e - b * a.max_chunks;
         }
+        if (b < 0) return;                         // past the last work item
+        b = __builtin_amdgcn_readfirstlane(b);
+        chunk = __builtin_amdgcn_readfirstlane(chunk);
+        L = min(max(a.seqlens_k[b], 0), a.capacity);
     } else {
-        int n, ahead, total;
-        rank_block(a, 0, lane, n, ahead, total);
+        int n, ahead, total, L_lane;
+        rank_block(a, 0, lane, n, ahead, total, L_lane);
         const unsigned long long hit = __ballot(n > 0 && item >= ahead && item < ahead + n);
-        if (hit) {
-            const int src = __ffsll((long long)hit) - 1;
-            b = src;
-            chunk = item - __shfl(ahead, src);
-        }
+        if (!hit) return;                          // past the last work item
+        b = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+        chunk = item - __builtin_amdgcn_readlane(ahead, b);
+        L = __builtin_amdgcn_readlane(L_lane, b);  // the length the ranking read
     }
-    if (b < 0) return;                             // past the last work item
-    b = __builtin_amdgcn_readfirstlane(b);         // uniform (shuffle results are not provably so)
-    chunk = __builtin_amdgcn_readfirstlane(chunk);
-    int lo, L, nchunks, C;
-    visible_range(a, b, lo, L);
+    int nchunks, C;
+    const int lo = visible_lo(a, L);
     chunking(a, lo, L, nchunks, C);
     const int k0 = chunk_origin(a, lo) + chunk * C;
     const int h0 = kvh * a.group + hg * GT;        // first query head of this workgroup
@@ -462,9 +470,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             l_part *= alpha_my;
         }
         // P of head my_g for this lane's keys, into the wavefront's LDS slot
-        float m_my = m_ref[0];
+        // (the reads go through readfirstlane, which the values allow: as plain
+        // reads of m_ref the compiler turns this choice into one indexed read
+        // and moves m_ref out of registers into LDS)
+        auto uni = [](float x) __attribute__((always_inline)) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+        };
+        float m_my = uni(m_ref[0]);
 #pragma unroll
-        for (int g = 1; g < GT; ++g) m_my = (my_g == g) ? m_ref[g] : m_my;
+        for (int g = 1; g < GT; ++g) m_my = (my_g == g) ? uni(m_ref[g]) : m_my;
         const float m_use = (m_my == -INFINITY) ? 0.f : m_my;
 #pragma unroll
         for (int p = 0; p < SP; ++p) {
@@ -614,8 +628,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void decode_plan_kernel(DecodeArgs a)
     int base = 0;
     for (int r0 = 0; r0 < a.batch; r0 += NW * 64) {
         const int b0 = r0 + wave * 64;
-        int n = 0, ahead = 0, total = 0;
-        if (b0 < a.batch) rank_block(a, b0, lane, n, ahead, total);
+        int n = 0, ahead = 0, total = 0, L_lane;
+        if (b0 < a.batch) rank_block(a, b0, lane, n, ahead, total, L_lane);
         if (lane == 0) block_total[wave] = total;
         __syncthreads();
         int excl = base, round_total = 0;
