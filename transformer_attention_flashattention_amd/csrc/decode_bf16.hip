@@ -42,6 +42,9 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
@@ -106,6 +109,21 @@ __device__ __forceinline__ float across_groups_sum(float x) {
     x += xor8(x);
     x += xor16(x);
     return x + xor32(x);
+}
+
+// Max / sum over the 16 lanes of each row (DPP inside the row); every lane of
+// the row gets the result.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false));      // quad_perm [1,0,3,2]
+    x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false));      // quad_perm [2,3,0,1]
+    x = fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false));     // row_half_mirror
+    return fmaxf(x, __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false));  // row_mirror
+}
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);
+    return x + __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false);
 }
 
 // Keys [lo, L) of sequence b are visible to its decode query.
@@ -196,6 +214,11 @@ template <> struct H16<false> {
     static __device__ __forceinline__ unsigned from_e4m3(unsigned w) {
         return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
     }
+    // 16 x 16 x 32 matrix product, fp32 accumulate
+    static __device__ __forceinline__ f32x4 mma(u32x4 x, u32x4 y, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                       __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+    }
 };
 template <> struct H16<true> {
     using t = _Float16;
@@ -220,6 +243,10 @@ template <> struct H16<true> {
     static __device__ __forceinline__ unsigned from_e4m3(unsigned w) {
         return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
     }
+    static __device__ __forceinline__ f32x4 mma(u32x4 x, u32x4 y, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                      __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+    }
 };
 
 // D: head_dim; GT: query heads per workgroup (all of one KV head's group, or
@@ -228,6 +255,20 @@ template <> struct H16<true> {
 // E4M3 codes with one scale per KV head each.  Chunk lengths are multiples of
 // NWAVES * KT.  KT: keys per wavefront tile.  F16: q and o are IEEE half
 // (and so is P in the P.V products) instead of bf16.
+//
+// With an FP8 cache the scores come from the matrix cores instead: per 16
+// keys, D / 32 products v_mfma_f32_16x16x32 of Q (rows: the GT query heads,
+// the other rows zero) with K^T (columns: the 16 keys), K's codes converted
+// to bf16 in registers.  The product wants lane l to hold key l % 16 and the
+// dims at 64 p + 16 (l / 16) .. +16 (p < D / 64); Q's operand holds the same
+// dims of head l % 16 (a dot product may sum its dims in any order, so the
+// same dims on both sides is all it needs).  Loaded that way, each load
+// instruction would cover 64-byte pieces of 16 rows, which stream markedly
+// slower than whole rows; so K is loaded in whole rows, as for the vector
+// path, and each wavefront passes its tile through a private LDS slot (16-byte
+// chunks XOR-swizzled by key) to read it back in the product's layout.
+// Lanes 0-15 then hold the GT scores of their key; the vector path's dot
+// products and lane sums per key (the bulk of its instructions) are gone.
 template <int D, int GT, bool ALIBI, bool PAGED, bool KV8, int KT, bool F16>
 __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     using H = H16<F16>;
@@ -238,9 +279,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int VKP = 64 / VL;             // keys per value pass
     constexpr int VP = KT / VKP;             // value passes per tile
     static_assert(GT <= SL && (SL == 4 || SL == 8), "layout");
+    constexpr bool QKM = KV8;                // scores on the matrix cores (FP8 cache)
+    constexpr int NM = D / 32;               // QKM: products per 16 keys
+    constexpr int NG = KT / 16;              // QKM: 16-key groups per tile
+    static_assert(!QKM || (KT % 16 == 0 && GT <= 4 && D % 64 == 0), "matrix-core score layout");
     static_assert(kDecodeChunkUnit % (NWAVES * KT) == 0, "chunks hold whole tile rounds");
 
     __shared__ __attribute__((aligned(16))) float pw[NWAVES][KT][GT];   // P, per wavefront
+    constexpr int CH = D / 16;                                           // 16-byte chunks of an FP8 row
+    __shared__ u32x4 kst[QKM ? NWAVES : 1][QKM ? KT * CH : 1];          // QKM: K tile, per wavefront
     __shared__ __attribute__((aligned(16))) float mo[NWAVES][GT][D];    // merge: P.V
     __shared__ float mml[NWAVES][GT][2];                                 // merge: (m, l)
 
@@ -304,16 +351,33 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     // (8 bf16 pairs): bf16 keys, dims 8 s_sub .. +8 and D/2 + 8 s_sub .. +8
     // (each key load instruction then covers one contiguous half of every
     // row); FP8 keys, dims 16 s_sub .. +16 (one 16-byte load per row piece)
-    unsigned qr[GT][8];
+    // (matrix-core scores: qr[m] is product m's operand, 8 dims of head
+    // qrow = l % 16 starting at qm_dim(m); zero for rows past GT)
+    const int qrow = lane & 15, qgrp = lane >> 4;
+    auto qm_dim = [&](int m) { return 64 * (m >> 1) + 16 * qgrp + 8 * (m & 1); };
+    constexpr int QA = QKM ? NM : GT, QB = QKM ? 4 : 8;
+    unsigned qr[QA][QB];
+    if constexpr (QKM) {
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-        const unsigned short *qp = (const unsigned short *)a.q + b * a.q_sb + (h0 + g) * a.q_sh
-                                   + s_sub * (KV8 ? 16 : 8);
-        const u32x4 x0 = *(const u32x4 *)qp, x1 = *(const u32x4 *)(qp + (KV8 ? 8 : D / 2));
+        for (int m = 0; m < NM; ++m) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow < GT)
+                x = *(const u32x4 *)((const unsigned short *)a.q + b * a.q_sb + (h0 + qrow) * a.q_sh
+                                     + qm_dim(m));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qr[g][i] = x0[i];
-            qr[g][4 + i] = x1[i];
+            for (int i = 0; i < 4; ++i) qr[m][i] = x[i];
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const unsigned short *qp = (const unsigned short *)a.q + b * a.q_sb + (h0 + g) * a.q_sh
+                                       + s_sub * 8;
+            const u32x4 x0 = *(const u32x4 *)qp, x1 = *(const u32x4 *)(qp + D / 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qr[g][i] = x0[i];
+                qr[g][4 + i] = x1[i];
+            }
         }
     }
 
@@ -324,15 +388,26 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         const int rhalf = a.rotary_dim / 2;
         const float *cr = a.rope_cos + (int64_t)(L - 1) * rhalf;
         const float *sr = a.rope_sin + (int64_t)(L - 1) * rhalf;
+        auto turn = [&](unsigned &w, int pr) __attribute__((always_inline)) {
+            const float c = cr[pr], sn = sr[pr];
+            const float x = H::lo(w), y = H::hi(w);
+            w = H::pack(__builtin_fmaf(x, c, -y * sn), __builtin_fmaf(x, sn, y * c));
+        };
+        if constexpr (QKM) {
+            if (qrow < GT) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int pr = KV8 ? 8 * s_sub + k : (k < 4 ? 4 * s_sub + k : D / 4 + 4 * s_sub + (k - 4));
-            if (pr < rhalf) {
-                const float c = cr[pr], sn = sr[pr];
+                for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    const float x = H::lo(qr[g][k]), y = H::hi(qr[g][k]);
-                    qr[g][k] = H::pack(__builtin_fmaf(x, c, -y * sn), __builtin_fmaf(x, sn, y * c));
+                    for (int w = 0; w < 4; ++w)
+                        if (qm_dim(m) / 2 + w < rhalf) turn(qr[m][w], qm_dim(m) / 2 + w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int pr = k < 4 ? 4 * s_sub + k : D / 4 + 4 * s_sub + (k - 4);
+                if (pr < rhalf) {
+#pragma unroll
+                    for (int g = 0; g < GT; ++g) turn(qr[g][k], pr);
                 }
             }
         }
@@ -341,6 +416,9 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     // running state (m, the reference, is uniform across the wavefront)
     float m_ref[GT], o[GT][8];
     float l_part = 0.f;                                // this lane's share of the sum of head my_g
+    float l_acc[GT];                                   // QKM: this lane's share of every head's sum
+#pragma unroll
+    for (int g = 0; g < GT; ++g) l_acc[g] = 0.f;
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
         m_ref[g] = -INFINITY;
@@ -380,11 +458,11 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     // (one uniform load) and addresses the rows inside it.
     // K: two 16-byte pieces per lane and pass (bf16) or one (FP8); V: 8 dims
     // per lane, 16 bytes (bf16) or 8 bytes (FP8)
-    constexpr int KPC = KV8 ? 1 : 2;
+    constexpr int KA = SP, KB = KV8 ? 1 : 2;
     using VVec = typename std::conditional<KV8, u32x2, u32x4>::type;
-    u32x4 kb[NBUF][SP][KPC];
+    u32x4 kb[NBUF][KA][KB];
     VVec vb[NBUF][VP];
-    auto load = [&](int t, u32x4 (&kt)[SP][KPC], VVec (&vt)[VP]) __attribute__((always_inline)) {
+    auto load = [&](int t, u32x4 (&kt)[KA][KB], VVec (&vt)[VP]) __attribute__((always_inline)) {
         const int t0 = tile_key0(t);
         const char *kbase = Kp, *vbase = Vp;
         int row0 = 0;                                  // logical key of row 0 at kbase
@@ -412,35 +490,66 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             vt[p] = load_nt<VVec>(vbase, (unsigned)(j - row0) * v_row + v_sub * 8 * ES);
         }
     };
-    auto compute = [&](int t, const u32x4 (&kt)[SP][KPC], const VVec (&vt)[VP]) __attribute__((always_inline)) {
+    auto compute = [&](int t, const u32x4 (&kt)[KA][KB], const VVec (&vt)[VP]) __attribute__((always_inline)) {
         const int t0 = tile_key0(t);
-        // scores of this lane's keys for every head
-        float s[SP][GT];
+        // scores for every head: of this lane's key in each score pass
+        // (vector path), or of key l % 16 of each 16-key group (matrix path,
+        // meaningful in lanes 0-15)
+        float s[KA][GT];
+        if constexpr (QKM) {
+            // the tile's rows into the wavefront's slot (lane: chunk s_sub of
+            // key p * SKP + s_key), chunk c of key k at c ^ (k % CH)
 #pragma unroll
-        for (int p = 0; p < SP; ++p) {
-            const int j = t0 + p * SKP + s_key;
-            const bool ok = j >= jlo && j < jhi;
-            // this lane's 16 dims of the key as 8 bf16 pairs, in qr's order
-            unsigned kw[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if constexpr (KV8) {
-                    kw[2 * i] = H::template from_e4m3<false>(kt[p][0][i]);
-                    kw[2 * i + 1] = H::template from_e4m3<true>(kt[p][0][i]);
-                } else {
-                    kw[i] = kt[p][0][i];
-                    kw[4 + i] = kt[p][KPC - 1][i];
-                }
+            for (int p = 0; p < SP; ++p) {
+                const int k = p * SKP + s_key;
+                kst[wave][k * CH + (s_sub ^ (k & (CH - 1)))] = kt[p][0];
             }
 #pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                float acc = 0.f;
+            for (int g16 = 0; g16 < NG; ++g16) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int k = g16 * 16 + qrow;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = H::dot(kw[i], qr[g][i], acc);
-                acc = group_sum<SL>(acc);
-                if constexpr (KV8) acc *= k_scale;
-                if constexpr (ALIBI) acc = __builtin_fmaf((float)(L - 1 - j), alibi_raw[g], acc);
-                s[p][g] = ok ? acc : -INFINITY;
+                for (int m = 0; m < NM; ++m) {
+                    const u32x4 w = kst[wave][k * CH + ((qgrp + 4 * (m >> 1)) ^ (k & (CH - 1)))];
+                    const int i = 2 * (m & 1);
+                    u32x4 kv;
+                    kv[0] = H::template from_e4m3<false>(w[i]);
+                    kv[1] = H::template from_e4m3<true>(w[i]);
+                    kv[2] = H::template from_e4m3<false>(w[i + 1]);
+                    kv[3] = H::template from_e4m3<true>(w[i + 1]);
+                    const u32x4 qv = {qr[m][0], qr[m][1], qr[m][2], qr[m][3]};
+                    acc = H::mma(qv, kv, acc);
+                }
+                const int j = t0 + g16 * 16 + qrow;
+                const bool ok = j >= jlo && j < jhi;
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    float v = acc[g] * k_scale;
+                    if constexpr (ALIBI) v = __builtin_fmaf((float)(L - 1 - j), alibi_raw[g], v);
+                    s[g16][g] = ok ? v : -INFINITY;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < SP; ++p) {
+                const int j = t0 + p * SKP + s_key;
+                const bool ok = j >= jlo && j < jhi;
+                // this lane's 16 dims of the key as 8 bf16 pairs, in qr's order
+                unsigned kw[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kw[i] = kt[p][0][i];
+                    kw[4 + i] = kt[p][1][i];
+                }
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = H::dot(kw[i], qr[g][i], acc);
+                    acc = group_sum<SL>(acc);
+                    if constexpr (ALIBI) acc = __builtin_fmaf((float)(L - 1 - j), alibi_raw[g], acc);
+                    s[p][g] = ok ? acc : -INFINITY;
+                }
             }
         }
         // tile max per head over the wavefront, then the lazy reference update
@@ -450,9 +559,10 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         for (int g = 0; g < GT; ++g) {
             float mt = s[0][g];
 #pragma unroll
-            for (int p = 1; p < SP; ++p) mt = fmaxf(mt, s[p][g]);
-            mt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                                __builtin_bit_cast(int, across_groups_max<SL>(mt))));
+            for (int p = 1; p < KA; ++p) mt = fmaxf(mt, s[p][g]);
+            // (matrix path: lane 0's row holds the keys; the other rows' values are not read)
+            mt = QKM ? row_max16(mt) : across_groups_max<SL>(mt);
+            mt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mt)));
             m_new[g] = fmaxf(m_ref[g], mt * c2);
             move |= m_new[g] > m_ref[g] + RESCALE_THRESHOLD;
         }
@@ -464,6 +574,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 const float alpha = mv ? __builtin_amdgcn_exp2f(m_ref[g] - m_new[g]) : 1.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+                l_acc[g] *= alpha;
                 if (g == my_g) alpha_my = alpha;
                 if (mv) m_ref[g] = m_new[g];
             }
@@ -476,19 +587,41 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         auto uni = [](float x) __attribute__((always_inline)) {
             return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
         };
-        float m_my = uni(m_ref[0]);
+        if constexpr (QKM) {
+            // lanes 0-15: P of every head for key l % 16 of each group
+            float m_use[GT];
 #pragma unroll
-        for (int g = 1; g < GT; ++g) m_my = (my_g == g) ? uni(m_ref[g]) : m_my;
-        const float m_use = (m_my == -INFINITY) ? 0.f : m_my;
+            for (int g = 0; g < GT; ++g) m_use[g] = (m_ref[g] == -INFINITY) ? 0.f : m_ref[g];
+            if (lane < 16) {
 #pragma unroll
-        for (int p = 0; p < SP; ++p) {
-            float sv = s[p][0];
+                for (int g16 = 0; g16 < NG; ++g16) {
+                    float pv[GT];
 #pragma unroll
-            for (int g = 1; g < GT; ++g) sv = (my_g == g) ? s[p][g] : sv;
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -m_use));
-            if (s_sub < GT) {
-                l_part += pv;
-                pw[wave][p * SKP + s_key][s_sub] = pv;
+                    for (int g = 0; g < GT; ++g) {
+                        pv[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g16][g], c2, -m_use[g]));
+                        l_acc[g] += pv[g];
+                    }
+                    float *dst = &pw[wave][g16 * 16 + qrow][0];
+                    if constexpr (GT == 4) *(float4 *)dst = make_float4(pv[0], pv[1], pv[2], pv[3]);
+                    else if constexpr (GT == 2) *(float2 *)dst = make_float2(pv[0], pv[1]);
+                    else dst[0] = pv[0];
+                }
+            }
+        } else {
+            float m_my = uni(m_ref[0]);
+#pragma unroll
+            for (int g = 1; g < GT; ++g) m_my = (my_g == g) ? uni(m_ref[g]) : m_my;
+            const float m_use = (m_my == -INFINITY) ? 0.f : m_my;
+#pragma unroll
+            for (int p = 0; p < SP; ++p) {
+                float sv = s[p][0];
+#pragma unroll
+                for (int g = 1; g < GT; ++g) sv = (my_g == g) ? s[p][g] : sv;
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -m_use));
+                if (s_sub < GT) {
+                    l_part += pv;
+                    pw[wave][p * SKP + s_key][s_sub] = pv;
+                }
             }
         }
         // P.V in the value layout, two keys at a time: a lane holds the same 8
@@ -575,7 +708,11 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             o[g][e] = x;
         }
     // row sum of head my_g: lanes with the same s_sub hold different keys
-    const float lsum = across_groups_sum<SL>(l_part);
+    // (matrix path: every head's sum, over the lanes of row 0)
+    const float lsum = QKM ? 0.f : across_groups_sum<SL>(l_part);
+    float lsum_g[GT];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) lsum_g[g] = QKM ? row_sum16(l_acc[g]) : 0.f;
     if (v_key == 0) {
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
@@ -583,7 +720,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             *(float4 *)&mo[wave][g][v_sub * 8 + 4] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
         }
     }
-    if (s_key == 0 && s_sub < GT) {
+    if constexpr (QKM) {
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                mml[wave][g][0] = m_ref[g];
+                mml[wave][g][1] = lsum_g[g];
+            }
+        }
+    } else if (s_key == 0 && s_sub < GT) {
         mml[wave][s_sub][0] = m_ref[0];
 #pragma unroll
         for (int g = 1; g < GT; ++g)
