@@ -121,3 +121,51 @@ def test_fp8_scales_and_growing_scores():
     dp.k_cache = np.where(np.isnan(k), workloads.FP8_E4M3_QNAN,
                           workloads.f32_to_fp8_e4m3_codes(np.nan_to_num(k).astype(np.float32)))
     _case(dp, "FP8 growing scores")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_every_e4m3_code_over_two_kv_heads(d):
+    """Two KV heads with their own V scales: their V rows hold all 256 codes
+    between them, one key per sequence, so each query head's O is its KV
+    head's V row times that head's scale: every code comes back as its exact
+    value, NaN codes as NaN (through the matrix-core P.V of 32-key tiles)."""
+    say(f"[fp8] all 256 codes over two KV heads, d={d}")
+    B = 256 // (2 * d)
+    codes = np.arange(256, dtype=np.uint8).reshape(B, 1, 2, d)
+    q = dev_tensor(workloads.f32_to_bf16_bits(np.zeros((B, 2, d), np.float32)), "bf16")
+    kc = fp8_tensor(np.full((B, 1, 2, d), 0x38, dtype=np.uint8))
+    vc = fp8_tensor(codes)
+    sk = torch.ones(B, dtype=torch.int32, device=DEV)
+    o, lse = fa.decode(q, kc, vc, sk, k_scale=[1.0, 1.0], v_scale=[1.0, 0.5])
+    torch.cuda.synchronize()
+    got = to_np(o).reshape(B, 2, d)
+    want = oracle.fp8_e4m3_value(codes.reshape(B, 2, d)) * np.array([1.0, 0.5])[None, :, None]
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin], want[fin]), np.nonzero(got[fin] != want[fin])
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(16, 4, 128), (8, 2, 64), (4, 4, 128)])
+def test_fp8_cache_with_a_head_stride(Hq, Hkv, d):
+    """The same cache read two ways: as stored and through a view whose head
+    stride is 2 d (every other slot of a wider buffer, NaN codes between).
+    Both match the oracle."""
+    dp = workloads.make_decode(76 + Hq + d, 7, Hq, Hkv, d, 1300, (1, 1300), "bf16",
+                               kv_dtype="fp8_e4m3")
+    _case(dp, f"FP8 Hq{Hq} Hkv{Hkv} d{d}")
+    B, cap = dp.k_cache.shape[:2]
+    views = []
+    for c in (dp.k_cache, dp.v_cache):
+        wide = np.full((B, cap, Hkv, 2 * d), workloads.FP8_E4M3_QNAN, dtype=np.uint8)
+        wide[..., :d] = c
+        views.append(fp8_tensor(wide)[..., :d])
+    assert views[0].stride(2) == 2 * d
+    q = dev_tensor(dp.q, dp.dtype)
+    sk = torch.from_numpy(dp.seqlens_k).to(DEV)
+    say(f"[fp8] through a view with head stride 2 d, Hq{Hq} Hkv{Hkv} d{d}")
+    o, lse = fa.decode(q, views[0], views[1], sk, scale=dp.scale,
+                       k_scale=torch.from_numpy(dp.k_scale).to(DEV),
+                       v_scale=torch.from_numpy(dp.v_scale).to(DEV))
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode_fp8(dp)
+    check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "FP8 head-strided view")

@@ -45,6 +45,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
 
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
@@ -269,8 +270,17 @@ template <> struct H16<true> {
 // chunks XOR-swizzled by key) to read it back in the product's layout.
 // Lanes 0-15 then hold the GT scores of their key; the vector path's dot
 // products and lane sums per key (the bulk of its instructions) are gone.
+// With 32-key tiles P.V goes to the matrix cores as well: O^T (D dims x the
+// heads) += V^T P^T, D / 16 products of 16 dims x 32 keys.  V passes through
+// a second LDS slot (rows as loaded, 16-byte chunks swizzled by key) and
+// comes back through the 8-bit transpose read ds_read_b64_tr_b8: in each
+// group of 16 lanes, lane i addresses 8 bytes of row i / 2 of an 8-row x
+// 16-byte block and receives column i of its 8 rows, i.e. one dim of 8
+// consecutive keys, the operand row the product wants.  P^T comes from LDS
+// in head-major order (8 consecutive keys of head l % 16 per lane).  Lane l
+// then holds O^T of dims 16 mm + 4 (l / 16) .. +4 for head l % 16.
 template <int D, int GT, bool ALIBI, bool PAGED, bool KV8, int KT, bool F16>
-__global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_split(DecodeArgs a) {
     using H = H16<F16>;
     constexpr int SL = D / 16;               // score layout: lanes per key (16 dims each)
     constexpr int SKP = 64 / SL;             // keys per score pass
@@ -283,11 +293,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     constexpr int NM = D / 32;               // QKM: products per 16 keys
     constexpr int NG = KT / 16;              // QKM: 16-key groups per tile
     static_assert(!QKM || (KT % 16 == 0 && GT <= 4 && D % 64 == 0), "matrix-core score layout");
+    constexpr bool PVM = QKM && KT == 32;    // P.V on the matrix cores too (32-key tiles)
+    constexpr int ND = D / 16;               // PVM: products per tile (16 dims each)
     static_assert(kDecodeChunkUnit % (NWAVES * KT) == 0, "chunks hold whole tile rounds");
 
     __shared__ __attribute__((aligned(16))) float pw[NWAVES][KT][GT];   // P, per wavefront
     constexpr int CH = D / 16;                                           // 16-byte chunks of an FP8 row
     __shared__ u32x4 kst[QKM ? NWAVES : 1][QKM ? KT * CH : 1];          // QKM: K tile, per wavefront
+    __shared__ u32x4 vst[PVM ? NWAVES : 1][PVM ? KT * CH : 1];          // PVM: V tile, per wavefront
+    __shared__ __attribute__((aligned(16))) float pwt[PVM ? NWAVES : 1][GT][PVM ? KT : 1];  // PVM: P, head-major
     __shared__ __attribute__((aligned(16))) float mo[NWAVES][GT][D];    // merge: P.V
     __shared__ float mml[NWAVES][GT][2];                                 // merge: (m, l)
 
@@ -415,6 +429,9 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
 
     // running state (m, the reference, is uniform across the wavefront)
     float m_ref[GT], o[GT][8];
+    f32x4 ot[PVM ? ND : 1];                            // PVM: O^T of this lane's dims and head
+#pragma unroll
+    for (int mm = 0; mm < (PVM ? ND : 1); ++mm) ot[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
     float l_part = 0.f;                                // this lane's share of the sum of head my_g
     float l_acc[GT];                                   // QKM: this lane's share of every head's sum
 #pragma unroll
@@ -504,6 +521,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 const int k = p * SKP + s_key;
                 kst[wave][k * CH + (s_sub ^ (k & (CH - 1)))] = kt[p][0];
             }
+            if constexpr (PVM) {
+                // V rows likewise (lane: 8 bytes, half v_sub % 2 of chunk v_sub / 2)
+                u32x2 *vs = (u32x2 *)&vst[wave][0];
+#pragma unroll
+                for (int p = 0; p < VP; ++p) {
+                    const int k = p * VKP + v_key;
+                    vs[(k * CH + ((v_sub >> 1) ^ (k & (CH - 1)))) * 2 + (v_sub & 1)] = vt[p];
+                }
+            }
 #pragma unroll
             for (int g16 = 0; g16 < NG; ++g16) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -567,7 +593,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             move |= m_new[g] > m_ref[g] + RESCALE_THRESHOLD;
         }
         if (move) {                                  // uniform across the wavefront
-            float alpha_my = 1.f;
+            float alpha_my = 1.f, alpha_q = 1.f;
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
                 const bool mv = m_new[g] > m_ref[g] + RESCALE_THRESHOLD;
@@ -576,9 +602,16 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
                 l_acc[g] *= alpha;
                 if (g == my_g) alpha_my = alpha;
+                alpha_q = (qrow == g) ? alpha : alpha_q;
                 if (mv) m_ref[g] = m_new[g];
             }
             l_part *= alpha_my;
+            if constexpr (PVM) {
+#pragma unroll
+                for (int mm = 0; mm < ND; ++mm)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ot[mm][e] *= alpha_q;
+            }
         }
         // P of head my_g for this lane's keys, into the wavefront's LDS slot
         // (the reads go through readfirstlane, which the values allow: as plain
@@ -601,10 +634,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                         pv[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g16][g], c2, -m_use[g]));
                         l_acc[g] += pv[g];
                     }
-                    float *dst = &pw[wave][g16 * 16 + qrow][0];
-                    if constexpr (GT == 4) *(float4 *)dst = make_float4(pv[0], pv[1], pv[2], pv[3]);
-                    else if constexpr (GT == 2) *(float2 *)dst = make_float2(pv[0], pv[1]);
-                    else dst[0] = pv[0];
+                    if constexpr (PVM) {
+#pragma unroll
+                        for (int g = 0; g < GT; ++g) pwt[wave][g][g16 * 16 + qrow] = pv[g];
+                    } else {
+                        float *dst = &pw[wave][g16 * 16 + qrow][0];
+                        if constexpr (GT == 4) *(float4 *)dst = make_float4(pv[0], pv[1], pv[2], pv[3]);
+                        else if constexpr (GT == 2) *(float2 *)dst = make_float2(pv[0], pv[1]);
+                        else dst[0] = pv[0];
+                    }
                 }
             }
         } else {
@@ -629,6 +667,28 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
         // per dim and v_dot2_f32_bf16 multiplies them with the pair of P values
         // (bf16, as for the matrix product of the prefill; fp32 accumulate)
         static_assert(VP % 2 == 0, "value passes come in pairs");
+        if constexpr (PVM) {
+            // P^T operand: keys 8 qgrp .. +8 of head qrow (zero past the heads)
+            const int hq = qrow < GT ? qrow : 0;
+            const float4 x = *(const float4 *)&pwt[wave][hq][8 * qgrp];
+            const float4 y = *(const float4 *)&pwt[wave][hq][8 * qgrp + 4];
+            u32x4 pb = {H::pack(x.x, x.y), H::pack(x.z, x.w), H::pack(y.x, y.y), H::pack(y.z, y.w)};
+            if (qrow >= GT) pb = u32x4{0u, 0u, 0u, 0u};
+            const char *vs = (const char *)&vst[wave][0];
+            const int row = 8 * qgrp + (qrow >> 1);
+#pragma unroll
+            for (int mm = 0; mm < ND; ++mm) {
+                const int off = row * D + ((mm ^ (row & (CH - 1))) << 4) + 8 * (qrow & 1);
+                const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) i32x2 *)(vs + off));
+                u32x4 va;
+                va[0] = H::template from_e4m3<false>((unsigned)w[0]);
+                va[1] = H::template from_e4m3<true>((unsigned)w[0]);
+                va[2] = H::template from_e4m3<false>((unsigned)w[1]);
+                va[3] = H::template from_e4m3<true>((unsigned)w[1]);
+                ot[mm] = H::mma(va, pb, ot[mm]);
+            }
+        } else {
 #pragma unroll
         for (int p = 0; p < VP; p += 2) {
             float pa[GT], pb[GT];
@@ -677,6 +737,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
                 }
             }
         }
+        }
     };
 
     // ---- tile loop: NBUF-1 tiles' loads are in flight during each compute ---
@@ -713,7 +774,14 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
     float lsum_g[GT];
 #pragma unroll
     for (int g = 0; g < GT; ++g) lsum_g[g] = QKM ? row_sum16(l_acc[g]) : 0.f;
-    if (v_key == 0) {
+    if constexpr (PVM) {
+        // O^T: lane l holds dims 16 mm + 4 qgrp .. +4 of head qrow
+        if (qrow < GT) {
+#pragma unroll
+            for (int mm = 0; mm < ND; ++mm)
+                *(float4 *)&mo[wave][qrow][16 * mm + 4 * qgrp] = make_float4(ot[mm][0], ot[mm][1], ot[mm][2], ot[mm][3]);
+        }
+    } else if (v_key == 0) {
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
             *(float4 *)&mo[wave][g][v_sub * 8] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
@@ -756,6 +824,19 @@ __global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
             a.ws_ml[row * 2 + 1] = lacc;
         }
     }
+}
+
+template <int D, int GT, bool ALIBI, bool PAGED, bool KV8, int KT, bool F16>
+__global__ __launch_bounds__(NTHREADS) void decode_split_kernel(DecodeArgs a) {
+    decode_split<D, GT, ALIBI, PAGED, KV8, KT, F16>(a);
+}
+
+// The FP8 cache's matrix-core accumulators would otherwise go to extra
+// accumulation registers, leaving two wavefronts per SIMD; asking for three
+// keeps them in the ordinary ones.
+template <int D, int GT, bool ALIBI, bool PAGED, int KT, bool F16>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_fp8_kernel(DecodeArgs a) {
+    decode_split<D, GT, ALIBI, PAGED, true, KT, F16>(a);
 }
 
 // Item table of a batch of more than 64 sequences, written once per call
@@ -870,9 +951,9 @@ void launch_split_kv(const DecodeArgs &a, dim3 grid, hipStream_t s) {
     if (!a.kv_fp8)
         hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, false, 16, F16>), grid, dim3(NTHREADS), 0, s, a);
     else if (tile_keys(a) == 32)
-        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 32, F16>), grid, dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((decode_split_fp8_kernel<D, GT, ALIBI, PAGED, 32, F16>), grid, dim3(NTHREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, GT, ALIBI, PAGED, true, 16, F16>), grid, dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((decode_split_fp8_kernel<D, GT, ALIBI, PAGED, 16, F16>), grid, dim3(NTHREADS), 0, s, a);
 }
 
 template <int D, bool F16, int GT, bool ALIBI>
