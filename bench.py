@@ -565,6 +565,10 @@ def main():
 PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 {opts} -d <out>/{sub} "
                "--output-format csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 "
                "--no-cpu-baseline")
+CTR1 = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA",
+        "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+CTR2 = ["SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY",
+        "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"]
 CALIB_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc {c} -d <out>/{sub} "
              "--output-format csv -- python3 /root/repo/bench.py --copy-calibration")
 # copy calibration: counter KiB per 1 GiB read (FETCH) or written (WRITE),
@@ -717,6 +721,43 @@ def summarize_profiles(out):
             ghz = float(np.median([x[1] / 8 / x[0] for x in vals]))
             lines.append(f"| {kname[:70]} | {len(vals)} | {dm / 1e3:.1f} | {cyc / 1e6:.3f} | {ghz:.3f} |")
         open(os.path.join(prof, "bench_workload_clock.md"), "w").write("\n".join(lines) + "\n")
+    # shader counters: two runs (each within the per-block counter limits)
+    c1 = glob.glob(f"{out}/ctr1/*/*_counter_collection.csv")
+    c2 = glob.glob(f"{out}/ctr2/*/*_counter_collection.csv")
+    if c1 and c2:
+        vals = collections.defaultdict(lambda: collections.defaultdict(float))
+        order = []
+        for run, f in (("ctr1", c1[0]), ("ctr2", c2[0])):
+            for r in csv.DictReader(open(f)):
+                k = _short(r["Kernel_Name"])
+                if not k.startswith(("prefill", "decode", "rope")):
+                    continue
+                if k not in order:
+                    order.append(k)
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and run == "ctr2":
+                    continue
+                vals[k][(r["Counter_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+        lines = [f"# Shader counters: {wl}", "",
+                 "Two runs (the counters of one run stay within the per-block limits):", "",
+                 "    " + PROFILE_CMD.format(opts="--pmc " + " ".join(CTR1), sub="ctr1"),
+                 "    " + PROFILE_CMD.format(opts="--pmc " + " ".join(CTR2), sub="ctr2"), "",
+                 "Values are per dispatch (averaged over the dispatches of each kernel), summed over "
+                 "the chip as the counters report them.  Ratios: VALU and LDS instructions per MFMA "
+                 "instruction, and the share of wave cycles spent waiting (SQ_WAIT_ANY / "
+                 "SQ_WAVE_CYCLES)."]
+        for k in order:
+            per = collections.defaultdict(list)
+            for (c, _), v in vals[k].items():
+                per[c].append(v)
+            mean = {c: float(np.mean(v)) for c, v in per.items()}
+            lines += ["", f"## {k}", "", "| counter | value |", "|---|---|"]
+            lines += [f"| {c} | {mean[c]:.0f} |" for c in sorted(mean)]
+            if mean.get("SQ_INSTS_MFMA"):
+                lines.append(f"| VALU / MFMA | {mean.get('SQ_INSTS_VALU', 0) / mean['SQ_INSTS_MFMA']:.2f} |")
+                lines.append(f"| LDS / MFMA | {mean.get('SQ_INSTS_LDS', 0) / mean['SQ_INSTS_MFMA']:.2f} |")
+            if mean.get("SQ_WAVE_CYCLES"):
+                lines.append(f"| wait share | {mean.get('SQ_WAIT_ANY', 0) / mean['SQ_WAVE_CYCLES']:.2f} |")
+        open(os.path.join(prof, "bench_workload_counters.md"), "w").write("\n".join(lines) + "\n")
     print(open(os.path.join(prof, "bench_workload_kernel_trace.md")).read())
 
 
