@@ -77,6 +77,21 @@ fa_status check_rope(int rotary_dim, int max_pos, const float *c, const float *s
         if (_s != FA_OK) return _s;       \
     } while (0)
 
+// Compute units of the device a stream belongs to (cached per device), or -1.
+int compute_units(hipStream_t s) {
+    static int cached[64];
+    int dev = 0;
+    if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return -1;
+    if (dev < 0 || dev >= 64) return -1;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return -1;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // Decode: query heads per workgroup (a divisor of the GQA group, at most 4).
 int decode_heads_per_wg(int group) {
     if (group % 4 == 0) return 4;
@@ -317,6 +332,13 @@ fa_status fa_prefill_fwd(const fa_prefill_params *p, void *hip_stream) {
         return fail(FA_ERR_UNSUPPORTED, "grid too large");
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    // packed GQA without biases: one workgroup per CU walks the work items
+    // (the kernel holds one workgroup per CU)
+    if (a.gqa_pack > 1 && !p->alibi_slopes && p->rotary_dim == 0 && !p->attn_mask) {
+        const int cus = compute_units(s);
+        if (cus < 0) return fail(FA_ERR_HIP, "cannot query the device of the stream");
+        a.persist_wgs = cus;
+    }
     if (ws_need > 0 && p->seqlen_k > 0) {
         // bf16 with RoPE: rotate K once into the workspace, then attend to it
         fa::RopeKArgs r{};

@@ -25,6 +25,7 @@ struct PrefillArgs {
     float scale;                   // softmax_scale
     int32_t num_q_tiles;           // position blocks per sequence (16-bit path: of 256 / gqa_pack)
     int32_t gqa_pack;              // 16-bit path: query heads of one KV head per workgroup
+    int32_t persist_wgs;           // packed 16-bit path: workgroups of the persistent form (0: off)
     const float *alibi;            // ALiBi slopes [heads_q] or null
     const float *rope_cos, *rope_sin;  // RoPE tables [max_pos, rotary_dim / 2], or null
     int32_t rotary_dim;            // 0 = no RoPE

@@ -220,15 +220,33 @@ __device__ __forceinline__ void lds_dma16(const char *g, char *l) {
                  : "memory", "m0");
 }
 
+// The same load with a wavefront-uniform base address (in SGPRs) and a 32-bit
+// per-lane offset, which holds one VGPR per load instead of two.
+__device__ __forceinline__ void lds_dma16_s(const char *base, unsigned off, char *l) {
+    const unsigned la = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)l;
+    // the base is the same in every lane; readfirstlane makes that visible,
+    // so that it lives in SGPRs as the instruction's base operand requires
+    const uint64_t bu = (uint64_t)(uintptr_t)base;
+    base = (const char *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((unsigned)(bu >> 32)) << 32) |
+                                     (unsigned)__builtin_amdgcn_readfirstlane((unsigned)bu));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(la))
+                 : "memory", "m0");
+}
+
 // D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores;
 // ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated);
 // MASK: add an explicit additive mask read from memory; F16: the inputs are
 // IEEE half instead of bf16; PACK: a.gqa_pack query heads share the
-// workgroup (without it one head, and the work-item arithmetic is constant).
-template <int D, bool ALIBI, bool ROPE, bool MASK, bool F16, bool PACK>
+// workgroup (without it one head, and the work-item arithmetic is constant);
+// PERSIST (with PACK, no biases): one workgroup per CU walks the work items
+// (see below) instead of one workgroup per item.
+template <int D, bool ALIBI, bool ROPE, bool MASK, bool F16, bool PACK, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
+    static_assert(!PERSIST || (PACK && !ALIBI && !ROPE && !MASK && D == 128), "persistent form: packed, no biases");
     using T = Tile<D>;
     using E = E16<F16>;
     using v8 = typename E::v8;
@@ -250,25 +268,50 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- work item --------------------------------------------------------
     const int GP = PACK ? a.gqa_pack : 1;             // query heads per workgroup
+    auto locate = [&](unsigned wi, int &rank, int &b, int &h, int &kvh) __attribute__((always_inline)) {
+        if constexpr (PACK) {
+            const int slices = a.group / GP;          // workgroups per (position block, KV head)
+            const int units = a.batch * a.heads_kv * slices;
+            rank = wi / units;
+            const int unit = wi - rank * units;
+            b = unit / (a.heads_kv * slices);
+            const int kvh_slice = unit - b * (a.heads_kv * slices);
+            kvh = kvh_slice / slices;
+            // this wavefront's query head (uniform across it)
+            h = __builtin_amdgcn_readfirstlane(kvh * a.group + (kvh_slice - kvh * slices) * GP + wave % GP);
+        } else {
+            const int bh_count = a.batch * a.heads_q;
+            rank = wi / bh_count;
+            const int bh = wi - rank * bh_count;
+            b = bh / a.heads_q;
+            h = bh - b * a.heads_q;
+            kvh = h / a.group;
+        }
+    };
+    // PERSIST: G workgroups (one per CU) take the items in rounds of G, in
+    // snake order (round r: workgroup w takes r G + w, or r G + G - 1 - w
+    // when r is odd), which keeps the heavy-first order of the items balanced
+    // across workgroups.  Once an item's tile loop is done, its LDS tiles are
+    // free: each wavefront loads its 32 rows of the next item's Q into 8 KiB
+    // of them (direct-to-LDS, 16-byte chunks XOR-swizzled by row) before it
+    // writes the current item's O, so the Q load overlaps the O write
+    // instead of starting the next item.
+    const int n_items = PERSIST ? a.num_q_tiles * (a.heads_q / GP) * a.batch : 0;
+    auto item_of = [&](int r) __attribute__((always_inline)) {
+        const int G = (int)gridDim.x, w = (int)blockIdx.x;
+        return r * G + ((r & 1) ? G - 1 - w : w);
+    };
+    // wavefront w's Q staging area: half w % 2 of tile buffer w / 2
+    auto q_stage = [&]() __attribute__((always_inline)) {
+        char *buf = (wave >> 1) == 0 ? sK0 : (wave >> 1) == 1 ? sK1 : (wave >> 1) == 2 ? sV0 : sV1;
+        return buf + (wave & 1) * 8192;
+    };
+    bool have_next = false;
+    for (int round = 0;; ++round) {
+    const unsigned wi = PERSIST ? (unsigned)item_of(round) : blockIdx.x;
+    if (PERSIST && (int)wi >= n_items) break;
     int rank, b, h, kvh;
-    if constexpr (PACK) {
-        const int slices = a.group / GP;              // workgroups per (position block, KV head)
-        const int units = a.batch * a.heads_kv * slices;
-        rank = blockIdx.x / units;
-        const int unit = blockIdx.x - rank * units;
-        b = unit / (a.heads_kv * slices);
-        const int kvh_slice = unit - b * (a.heads_kv * slices);
-        kvh = kvh_slice / slices;
-        // this wavefront's query head (uniform across it)
-        h = __builtin_amdgcn_readfirstlane(kvh * a.group + (kvh_slice - kvh * slices) * GP + wave % GP);
-    } else {
-        const int bh_count = a.batch * a.heads_q;
-        rank = blockIdx.x / bh_count;
-        const int bh = blockIdx.x - rank * bh_count;
-        b = bh / a.heads_q;
-        h = bh - b * a.heads_q;
-        kvh = h / a.group;
-    }
+    locate(wi, rank, b, h, kvh);
     const int qtile = a.causal ? (a.num_q_tiles - 1 - rank) : rank;
 
     int Lq = a.seqlen_q, Lk = a.seqlen_k;
@@ -329,7 +372,25 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- Q fragment (B operand), zero for rows outside the valid length ---
     v8 qf[KSTEPS];
-    {
+    if (PERSIST && have_next) {
+        // staged by the previous item; then every wavefront has its Q before
+        // the first K tile goes into the same buffers
+        wait_loads();
+        const bool ok = qi < Lq;
+        const char *stage = q_stage();
+        // (lane indices through an empty asm: the per-lane offsets are then
+        // computed here, not hoisted out of the item loop into registers that
+        // would stay live across every tile loop)
+        int r = l32, hf = half;
+        asm volatile("" : "+v"(r), "+v"(hf));
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            u32x4 v = *(const u32x4 *)(stage + r * 256 + (((2 * ks + hf) ^ (r & 15)) << 4));
+            if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+            qf[ks] = __builtin_bit_cast(v8, v);
+        }
+        phase_barrier();
+    } else {
         const bool ok = qi < Lq && (!ROPE || qi >= q_first);
         const unsigned short *row = Qp + (int64_t)qi * a.q_ss + half * 8;
 #pragma unroll
@@ -670,6 +731,41 @@ void prefill_bf16_kernel(PrefillArgs a) {
         phase_barrier();
     }
 
+    // ---- PERSIST: the next item's Q rows into LDS, before O is written ----
+    // Every wavefront is past the tile loop's last barrier, so no one reads
+    // the tile buffers any more.  Rows past the valid length load a valid
+    // row and are zeroed when read.  The load overlaps the O write.
+    if constexpr (PERSIST) {
+        // (the empty asm hides that nx is the next round's item, so the
+        // compiler does not carry this set-up across the next item's loop)
+        int nx = item_of(round + 1);
+        asm volatile("" : "+s"(nx));
+        have_next = nx < n_items;
+        if (have_next) {
+            int r2, b2, h2, kvh2;
+            locate((unsigned)nx, r2, b2, h2, kvh2);
+            const int qt2 = a.causal ? (a.num_q_tiles - 1 - r2) : r2;
+            int Lq2 = a.seqlen_q;
+            if (a.seqlens_q) Lq2 = min(max(a.seqlens_q[b2], 0), a.seqlen_q);
+            const int q0w2 = qt2 * wg_rows + (wave / GP) * 32;
+            // uniform base at the first row loaded; rows past the valid length
+            // clamp to the last valid row (row 0 of an empty sequence)
+            const int rb = max(0, min(q0w2, Lq2 - 1));
+            const char *qb = (const char *)((const unsigned short *)a.q + b2 * a.q_sb + h2 * a.q_sh +
+                                            (int64_t)rb * a.q_ss);
+            char *stage = q_stage();
+            int ln = lane;                                    // (as above: not hoisted)
+            asm volatile("" : "+v"(ln));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = i * 4 + (ln >> 4);              // row of the 32 this lane's chunk is in
+                const int c = (ln & 15) ^ (r & 15);           // the chunk that belongs at this slot
+                const int row = max(0, min(q0w2 + r, Lq2 - 1));
+                lds_dma16_s(qb, (unsigned)((row - rb) * a.q_ss * 2) + (c << 4), stage + i * 1024);
+            }
+        }
+    }
+
     // ---- epilogue: normalise once, write O (bf16, RNE) and LSE -------------
     const float l_tot = pair_sum(l_run);
     const bool row_ok = qi < Lq && l_tot > 0.f;
@@ -691,6 +787,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
             lrow[qi] = row_ok ? (m_ref + log2f(l_tot)) * LN2 : -INFINITY;
         }
     }
+    if constexpr (!PERSIST) break;
+    }   // items
 }
 
 
@@ -699,12 +797,16 @@ void launch_mask(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
     // GQA packing is built for the bf16 d = 128 kernels; elsewhere one head
     // per workgroup (valid for any group)
     constexpr bool CAN_PACK = D == 128 && !F16;
-    if (a.gqa_pack > 1 && CAN_PACK) {
-        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, CAN_PACK>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, CAN_PACK>), grid, block, 0, s, a);
+    constexpr bool CAN_PERSIST = CAN_PACK && !ALIBI && !ROPE;
+    if (a.gqa_pack > 1 && CAN_PERSIST && !a.mask && a.persist_wgs > 0 && grid.x > (unsigned)a.persist_wgs) {
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, F16, CAN_PACK, CAN_PERSIST>),
+                           dim3(a.persist_wgs), block, 0, s, a);
+    } else if (a.gqa_pack > 1 && CAN_PACK) {
+        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, CAN_PACK, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, CAN_PACK, false>), grid, block, 0, s, a);
     } else {
-        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, false>), grid, block, 0, s, a);
+        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, false, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, false, false>), grid, block, 0, s, a);
     }
 }
 
