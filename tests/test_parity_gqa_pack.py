@@ -5,7 +5,9 @@ positions each).  Against the fp64 oracle on every output, for groups of 2,
 problems and with every bias at once; and bit for bit against the same
 problem run as plain multi-head attention (K and V copied once per query
 head), which takes the one-head-per-workgroup kernel: each wavefront visits
-the same key tiles in the same order either way.
+the same key tiles in the same order either way.  With more work items
+than CUs the packed kernel runs in its persistent form (one workgroup per
+CU walking the items); that form is checked the same two ways.
 """
 import numpy as np
 import pytest
@@ -93,3 +95,46 @@ def test_packed_bit_identical_to_per_head_kernel(group, kw):
     o2, l2 = run_prefill(mha)
     assert np.array_equal(o1, o2), "packed GQA output differs from the per-head kernel"
     assert np.array_equal(l1, l2), "packed GQA LSE differs from the per-head kernel"
+
+
+def _persistent_problem(seed, **kw):
+    # B2 Hq32 Hkv8 N1100, group 4: 4 heads x 64 positions per workgroup, so
+    # 18 position blocks x 8 KV heads x 2 sequences = 288 work items, more than
+    # the CUs of the device: the persistent form runs (one workgroup per CU,
+    # a second, partial round in snake order)
+    return workloads.make_prefill(seed, 2, 1100, 1100, 32, 8, 128, "bf16", **kw)
+
+
+@pytest.mark.parametrize("kind", ["causal", "window", "varlen_with_empty"])
+def test_persistent_packed_form(kind):
+    """The persistent form of the packed kernel (more work items than CUs)
+    against the oracle on every output, including an empty sequence whose
+    query rows the next-item Q staging clamps."""
+    assert torch.cuda.get_device_properties(0).multi_processor_count < 288
+    if kind == "causal":
+        p = _persistent_problem(360, causal=True)
+    elif kind == "window":
+        p = _persistent_problem(361, causal=True, window_left=300)
+    else:
+        p = _persistent_problem(362, causal=True, seqlens_k_range=(1, 1100), seqlens_q_equal_k=True,
+                                poison_padding=True)
+        nan = workloads.f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+        p.seqlens_k[0] = 0
+        p.seqlens_q[0] = 0
+        p.q[0] = nan
+        p.k[0] = nan
+        p.v[0] = nan
+    _case(p, f"persistent {kind}")
+
+
+def test_persistent_form_bit_identical_to_per_head_kernel():
+    """The persistent packed kernel against plain MHA (K and V copied per
+    query head, one head per workgroup, one workgroup per item)."""
+    p = _persistent_problem(363, causal=True, window_left=500)
+    say("[gqa pack] persistent form, bit identity against the per-head kernel")
+    o1, l1 = run_prefill(p)
+    mha = workloads.PrefillProblem("bf16", p.q, np.repeat(p.k, 4, axis=2), np.repeat(p.v, 4, axis=2),
+                                   p.scale, p.causal, p.window_left, p.seqlens_q, p.seqlens_k)
+    o2, l2 = run_prefill(mha)
+    assert np.array_equal(o1, o2), "persistent packed output differs from the per-head kernel"
+    assert np.array_equal(l1, l2), "persistent packed LSE differs from the per-head kernel"
