@@ -453,25 +453,24 @@ def main():
                     **ms_stats(ms2), "algorithmic_flop": fl2, "algorithmic_bytes": by2,
                     "tflops": round(tf(fl2, ms2.mean()), 2),
                     "roofline": roofline("mfma", tf(fl2, ms2.mean()), PEAK_BF16_TFLOPS, "TFLOP/s",
-                                         measured_traffic(["prefill_bf16_kernel<64, false, false, false, false, false>"])),
+                                         measured_traffic([K_PREFILL_D64])),
                     "roofline_hbm": roofline("hbm", by2 / (ms2.mean() * 1e-3) / 1e9, PEAK_HBM_GBS,
                                              "GB/s")},
         "config3": {"workload": "B1 H32 N8192 d128 bf16 causal (the step's prefill)",
                     **ms_stats(pre_ms), "algorithmic_flop": flops, "algorithmic_bytes": by3,
                     "tflops": round(tflops, 2),
                     "roofline": roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                         measured_traffic(["prefill_bf16_kernel<128>"]))},
+                                         measured_traffic([K_PREFILL]))},
         "config4": {"workload": "B2 Hq32 Hkv8 N4096 d128 bf16 causal, window 1024",
                     **ms_stats(ms4), "algorithmic_flop": fl4, "algorithmic_bytes": by4,
                     "tflops": round(tf(fl4, ms4.mean()), 2),
                     "roofline": roofline("mfma", tf(fl4, ms4.mean()), PEAK_BF16_TFLOPS, "TFLOP/s",
-                                         measured_traffic(["prefill_bf16_kernel<128, false, false, false, false, true>"]))},
+                                         measured_traffic([K_PREFILL_GQA]))},
         "config5": {"workload": "decode B64 Hq32 Hkv8 d128 bf16, KV lengths U[512,8192] "
                                 f"(sum {int(np.sum(dp.seqlens_k))}) (the step's decode)",
                     **ms_stats(dec_ms), "algorithmic_bytes": dbytes, "gbs": round(gbs, 1),
                     "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
-                                         measured_traffic(["decode_split_kernel",
-                                                           "decode_combine_kernel<128>"]))},
+                                         measured_traffic([K_DECODE, K_COMBINE]))},
     }
 
     result = {
@@ -527,7 +526,8 @@ def main():
                    "frac_of_hbm_peak": round(fp8_bytes / (dec_f.mean() * 1e-3) / 1e9
                                              / PEAK_HBM_GBS, 4),
                    "speedup_vs_bf16_cache": round(float(dec_ms.mean() / dec_f.mean()), 3),
-                   "algorithmic_bytes": fp8_bytes, "calls": n_var},
+                   "algorithmic_bytes": fp8_bytes, "calls": n_var,
+                   "traffic": measured_traffic([K_DECODE_FP8, K_COMBINE])},
         "paged": {"page_size": page, "num_pages": int(pp.k_pool.shape[0]),
                   "decode_ms_mean": round(float(dec_p.mean()), 4),
                   "decode_gbs": round((dbytes + table_bytes) / (dec_p.mean() * 1e-3) / 1e9, 1),
@@ -567,6 +567,14 @@ def main():
 PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 {opts} -d <out>/{sub} "
                "--output-format csv -- python3 /root/repo/bench.py --steps 3 --warmup 1 "
                "--no-cpu-baseline")
+# kernels (exact template names of the kernel trace) whose counter-measured
+# HBM bytes the JSON line reports
+K_PREFILL = "prefill_bf16_kernel<128, false, false, false, false, false, false>"
+K_PREFILL_GQA = "prefill_bf16_kernel<128, false, false, false, false, true, true>"
+K_PREFILL_D64 = "prefill_bf16_kernel<64, false, false, false, false, false, false>"
+K_DECODE = "decode_split_kernel<128, 4, false, false, false, 16, false>"
+K_DECODE_FP8 = "decode_split_fp8_kernel<128, 4, false, false, 32, false>"
+K_COMBINE = "decode_combine_kernel<128, false>"
 CTR1 = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA",
         "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
 CTR2 = ["SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY",
@@ -674,16 +682,7 @@ def summarize_profiles(out):
                      "sources": srcs, "sources_sha256": sha(srcs)}
     pf = [CSRC + "prefill_bf16.hip", CSRC + "fa_internal.h"]
     dc = [CSRC + "decode_bf16.hip", CSRC + "fa_internal.h", CSRC + "fa_api.cpp"]
-    # the step's kernels under short keys (exact template names of the trace)
-    main_names = {"prefill_bf16_kernel<128>": "prefill_bf16_kernel<128, false, false, false, false, false>",
-                  "decode_split_kernel": "decode_split_kernel<128, 4, false, false, false, 16, false>",
-                  "decode_combine_kernel<128>": "decode_combine_kernel<128, false>"}
-    for key, kname in main_names.items():
-        if kname in fetch:
-            ent(key, kname, pf if key.startswith("prefill") else dc)
     for kname in fetch:
-        if kname in main_names.values():
-            continue
         if kname.startswith("prefill_bf16"):
             ent(kname, kname, pf)
         elif kname.startswith("prefill_f32"):
@@ -710,14 +709,14 @@ def summarize_profiles(out):
         lines = [f"# Shader clock under load: {wl}", "",
                  "GRBM_COUNT counts clock cycles of each of the 8 XCDs while a dispatch runs, so "
                  "GRBM_COUNT / 8 / duration is the average shader clock. Kernels shorter than "
-                 "about 20 us are left out (the count is too coarse there).", "",
+                 "100 us are left out (there the count and the duration are too coarse).", "",
                  "    " + PROFILE_CMD.format(opts="--pmc GRBM_COUNT GRBM_GUI_ACTIVE --kernel-trace",
                                              sub="clk"), "",
                  "| kernel | dispatches | average us (under counters) | cycles per XCD (M) | clock GHz |",
                  "|---|---|---|---|---|"]
         for kname, vals in sorted(per.items(), key=lambda kv: -np.mean([x[0] for x in kv[1]])):
             dm = float(np.mean([x[0] for x in vals]))
-            if dm < 20000:
+            if dm < 100000:
                 continue
             cyc = float(np.mean([x[1] for x in vals])) / 8
             ghz = float(np.median([x[1] / 8 / x[0] for x in vals]))
