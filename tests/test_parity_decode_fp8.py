@@ -65,7 +65,7 @@ def test_fp8_lengths_around_edges(chunk):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 128), (32, 4, 128), (8, 1, 128), (12, 4, 64),
-                                      (6, 2, 64)])
+                                      (6, 2, 64), (8, 4, 128), (4, 2, 64), (16, 2, 128)])
 def test_fp8_gqa_and_head_dim(Hq, Hkv, d):
     dp = workloads.make_decode(71 + Hq, 5, Hq, Hkv, d, 900, (1, 900), "bf16",
                                kv_dtype="fp8_e4m3")

@@ -200,3 +200,21 @@ def test_rope_k_pass_writes_only_its_workspace():
                               seqlens_q=p.seqlens_q, seqlens_k=p.seqlens_k,
                               rope=(cos_t, sin_t, 128, "bf16"))
     check(to_np(o), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16", "RoPE canaries")
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,rdim", [(8, 4, 128, 64), (4, 2, 64, 32), (8, 2, 64, 64)])
+def test_rope_decode_fp8_partial_rotary(Hq, Hkv, d, rdim):
+    """FP8 cache with RoPE over the first rdim dims only, for head dims 128
+    and 64 and GQA groups of 2 and 4: the query's rotated and unrotated dims
+    sit in the matrix-core operand layout of the FP8 path."""
+    from gpu_helpers import run_decode_fp8
+    say(f"[rope] decode fp8 Hq{Hq} Hkv{Hkv} d{d} rotary {rdim}")
+    cos_t, sin_t = tables(1000, rdim)
+    c, s = torch.from_numpy(cos_t).to(DEV), torch.from_numpy(sin_t).to(DEV)
+    dp = workloads.make_decode(140 + Hq + d + rdim, 5, Hq, Hkv, d, 1000, (1, 1000), "bf16",
+                               kv_dtype="fp8_e4m3")
+    o, lse = run_decode_fp8(dp, rope_cos=c, rope_sin=s)
+    ro, rl = oracle.decode(workloads.to_f64(dp.q, "bf16"), oracle.dequantize_kv(dp.k_cache, dp.k_scale),
+                           oracle.dequantize_kv(dp.v_cache, dp.v_scale), dp.seqlens_k, scale=dp.scale,
+                           rope_q=(cos_t, sin_t, rdim, "bf16"))
+    check(o, lse, ro, rl, "bf16", f"decode RoPE fp8 d{d} rotary {rdim}")
