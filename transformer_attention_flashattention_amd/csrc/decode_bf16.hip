@@ -24,7 +24,8 @@
 //     where P.V accumulates in fp32 registers (packed bf16 dot products over
 //     pairs of keys; P enters that product in bf16, its row sum in fp32).
 // The four wavefronts merge their (max, sum, P.V) once per chunk through LDS
-// and write the chunk's partial to the workspace.
+// and write the chunk's partial to the workspace.  With an FP8 cache both
+// products run on the matrix cores instead (see decode_split below).
 // Combine kernel -- one wavefront per (sequence, query head): merges the
 //   chunk partials with the log-sum-exp rule (M = max m_c; L = sum 2^(m_c-M)
 //   l_c; O = sum 2^(m_c-M) O_c / L; LSE = ln 2 (M + log2 L)), the same max
