@@ -218,11 +218,25 @@ def cpu_decode(dp, nbytes, info, repeats):
 # ---------------------------------------------------------------------------
 # GPU timing helpers
 # ---------------------------------------------------------------------------
-def time_calls(torch, fn, n, warm=3):
-    """Per-call HIP-event times (ms) of ``fn`` on the current stream."""
-    for _ in range(warm):
-        fn()
+def warm_up(torch, fns, warm, warm_ms):
+    """Untimed calls: at least ``warm`` rounds of ``fns`` and at least
+    ``warm_ms`` of wall time with the GPU kept busy.  After the host has left
+    the GPU idle (input generation), its clock takes milliseconds to come
+    back up; a fixed count of a short call ends before that."""
+    t0 = time.perf_counter()
+    k = 0
+    while k < warm or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for f in fns:
+            f()
+        k += 1
+        if k % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def time_calls(torch, fn, n, warm=3, warm_ms=25.0):
+    """Per-call HIP-event times (ms) of ``fn`` on the current stream."""
+    warm_up(torch, [fn], warm, warm_ms)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
     for e in ev:
         e[0].record()
@@ -232,14 +246,11 @@ def time_calls(torch, fn, n, warm=3):
     return np.array([e[0].elapsed_time(e[1]) for e in ev])
 
 
-def time_pairs(torch, fa_, fb_, n, warm=3):
+def time_pairs(torch, fa_, fb_, n, warm=3, warm_ms=25.0):
     """Per-call HIP-event times (ms) of ``fa_`` and ``fb_`` called alternately
     (a, b, a, b, ...), so that both see the same clock and the same preceding
     work."""
-    for _ in range(warm):
-        fa_()
-        fb_()
-    torch.cuda.synchronize()
+    warm_up(torch, [fa_, fb_], warm, warm_ms)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
     for e in ev:
         e[0].record()
@@ -327,7 +338,8 @@ def main():
     # (reported beside the steps, never as the value); measured first, so the
     # later measurements start on a GPU that is already busy.  The GPU idled
     # while the host drew the inputs, and its clock takes some milliseconds to
-    # come back up: 30 untimed calls (about 15 ms) go first.
+    # come back up: 30 untimed calls (at least 25 ms) go first, and every
+    # per-call timing below starts with at least 25 ms of untimed calls.
     n_b2b = 50
     pre_bb = time_calls(torch, lambda: fa.prefill(q, k, v, causal=True, scale=p.scale, out=o,
                                                    lse=lse), n_b2b, warm=30)
