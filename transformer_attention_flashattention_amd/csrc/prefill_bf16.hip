@@ -372,6 +372,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- Q fragment (B operand), zero for rows outside the valid length ---
     v8 qf[KSTEPS];
+    bool q_rot = false;                   // RoPE: this lane's row is loaded and gets turned
     if (PERSIST && have_next) {
         // staged by the previous item; then every wavefront has its Q before
         // the first K tile goes into the same buffers
@@ -399,20 +400,41 @@ void prefill_bf16_kernel(PrefillArgs a) {
             if (ok) v = *(const u32x4 *)(row + ks * 16);
             qf[ks] = __builtin_bit_cast(v8, v);
         }
-        // RoPE: the lane's 8 dims of a k-step are 4 adjacent pairs, turned by
-        // the angles of its row's position (qi + Lk - Lq >= 0 for the rows
-        // loaded); the result is rounded to bf16, the operand precision
+        q_rot = ROPE && ok;
+    }
+
+    // RoPE: the lane's 8 dims of a k-step are 4 adjacent pairs, turned by the
+    // angles of its row's position (qi + Lk - Lq >= 0 for the rows loaded);
+    // the result is rounded to bf16, the operand precision.  Every table read
+    // of the row is issued together with the first K tile's loads (one memory
+    // round trip; k-steps past rotary_dim read the row's last group of 4 pairs
+    // and leave their dims unturned).  The leading group turns its rows before
+    // the first barrier; the lagging group, whose first matrix step comes one
+    // phase later, turns them while the leading group runs that step.
+    float4 rope_c[ROPE ? KSTEPS : 1], rope_s[ROPE ? KSTEPS : 1];
+    auto rope_tables = [&]() __attribute__((always_inline)) {
         if constexpr (ROPE) {
-            if (ok) {
+            if (q_rot) {
                 const int rhalf = a.rotary_dim / 2;
                 const float *cr = a.rope_cos + (int64_t)(qi + offset) * rhalf;
                 const float *sr = a.rope_sin + (int64_t)(qi + offset) * rhalf;
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
+                    const int pl = min(ks * 8 + half * 4, rhalf - 4);
+                    rope_c[ks] = *(const float4 *)(cr + pl);
+                    rope_s[ks] = *(const float4 *)(sr + pl);
+                }
+            }
+        }
+    };
+    auto rotate_q = [&]() __attribute__((always_inline)) {
+        if constexpr (ROPE) {
+            if (q_rot) {
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
                     const int p0 = ks * 8 + half * 4;           // first pair of the 8 dims
                     if (2 * p0 < a.rotary_dim) {                 // rotary_dim: whole groups of 4 pairs
-                        const float4 c = *(const float4 *)(cr + p0);
-                        const float4 sn = *(const float4 *)(sr + p0);
+                        const float4 c = rope_c[ks], sn = rope_s[ks];
                         const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -424,7 +446,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 }
             }
         }
-    }
+    };
 
     // ---- HBM -> LDS: each wavefront writes LOADS_PER_WAVE x 1 KiB per tile --
     // For load i the lane's tile row and physical chunk are fixed; only the
@@ -702,8 +724,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // LDS buffer is named statically.
     const int nph = ntiles > 0 ? 2 * ntiles + 2 : 0;
     if (ntiles > 0) issue_k(0, sK0);
+    rope_tables();
+    if (grp == 0) rotate_q();
     wait_loads();
     __syncthreads();
+    if (grp != 0) rotate_q();
     for (int p = 0; p < nph; p += 4) {
         const int j = p >> 1;             // even tile index of this unrolled block
         // phase p (= 2j): leading: matrix(j) ; lagging: softmax(j-1)
