@@ -664,14 +664,23 @@ def summarize_profiles(out):
 
     # kernel trace
     rows = list(csv.DictReader(open(_one(f"{out}/kt/*/*_kernel_stats.csv"))))
+    # per-dispatch durations (for the median: the average also holds the
+    # first calls after the GPU idled, whose clock is still rising)
+    durs = collections.defaultdict(list)
+    for r in csv.DictReader(open(_one(f"{out}/kt/*/*_kernel_trace.csv"))):
+        durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = [f"# Kernel trace: {wl}", "",
              "Command (one warm-up step and three timed steps of bench.py, then everything else "
              "it times):", "", "    " + PROFILE_CMD.format(opts="--kernel-trace --stats", sub="kt"),
-             "", "Summarised by `python bench.py --summarize-profiles <out>`.", "",
-             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+             "", "Summarised by `python bench.py --summarize-profiles <out>` (the median from the "
+             "per-dispatch trace).", "",
+             "| kernel | calls | average us | median us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows:
+        d = durs.get(r["Name"])
+        med = f"{float(np.median(d)):.1f}" if d else "-"
         lines.append(f"| {_short(r['Name'])[:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} "
-                     f"| {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} "
+                     f"| {med} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} "
                      f"| {float(r['Percentage']):.1f}% |")
     open(os.path.join(prof, "bench_workload_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
 
