@@ -608,9 +608,9 @@ PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 {
                "--no-cpu-baseline")
 # kernels (exact template names of the kernel trace) whose counter-measured
 # HBM bytes the JSON line reports
-K_PREFILL = "prefill_bf16_kernel<128, false, false, false, false, false, false>"
-K_PREFILL_GQA = "prefill_bf16_kernel<128, false, false, false, false, true, true>"
-K_PREFILL_D64 = "prefill_bf16_kernel<64, false, false, false, false, false, false>"
+K_PREFILL = "prefill_bf16_kernel<128, false, false, 0, false, false, false>"
+K_PREFILL_GQA = "prefill_bf16_kernel<128, false, false, 0, false, true, true>"
+K_PREFILL_D64 = "prefill_bf16_kernel<64, false, false, 0, false, false, false>"
 K_DECODE = "decode_split_kernel<128, 4, false, false, false, 16, false>"
 K_DECODE_FP8 = "decode_split_fp8_kernel<128, 4, false, false, 32, false>"
 K_COMBINE = "decode_combine_kernel<128, false>"

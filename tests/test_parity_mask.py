@@ -16,11 +16,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _stored(m, dtype):
-    """The mask as stored (bf16 bits or fp32) and its exact float64 values."""
+    """The mask as stored (bf16 bits, half bits or fp32) and its exact float64 values."""
     if dtype == "bf16":
         bits = workloads.f32_to_bf16_bits(m.astype(np.float32))
         t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
         return t, workloads.bf16_bits_to_f32(bits).astype(np.float64)
+    if dtype == "f16":
+        h = np.ascontiguousarray(m, dtype=np.float32).astype(np.float16)
+        return torch.from_numpy(h), h.astype(np.float64)
     f = m.astype(np.float32)
     return torch.from_numpy(f), f.astype(np.float64)
 
@@ -69,6 +72,59 @@ def test_dense_random_mask_broadcasts(shape):
     m = rng.standard_normal(shape) * 2.0
     m[rng.random(shape) < 0.05] = -np.inf
     _case(p, m, f"dense mask {shape}")
+
+
+# Key masks (one row per batch and head, broadcast over the query rows: row
+# stride 0) take the matrix-core path: the mask value enters the scores as one
+# more k-step of the S product.
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv", [("bf16", 128, 8, 2), ("bf16", 64, 4, 4),
+                                             ("f16", 128, 4, 1), ("f16", 64, 6, 3)])
+def test_key_mask_per_head_random(dtype, d, Hq, Hkv):
+    """Random key-mask rows per batch and head (some -inf), causal, a ragged
+    key count, GQA (packed for bf16 d128), valid key lengths."""
+    p = workloads.make_prefill(130, 2, 300, 333, Hq, Hkv, d, dtype, causal=True,
+                               seqlens_k_range=(200, 333))
+    rng = np.random.default_rng(131)
+    m = rng.standard_normal((2, Hq, 1, 333)) * 3.0
+    m[rng.random(m.shape) < 0.1] = -np.inf
+    _case(p, m, f"key mask [2,{Hq},1,333] {dtype} d{d}")
+
+
+def test_key_mask_with_alibi_window():
+    p = workloads.make_prefill(132, 2, 400, 400, 4, 2, 128, "bf16", causal=True, window_left=150)
+    rng = np.random.default_rng(133)
+    m = rng.standard_normal((2, 1, 1, 400)) * 2.0
+    m[:, :, :, 390:] = -np.inf
+    _case(p, m, "key mask + ALiBi + window",
+          alibi_slopes=np.array([0.02, 0.05, 0.1, 0.2], dtype=np.float32))
+
+
+def test_key_mask_large_and_tiny_values():
+    """Magnitudes far from 1 (the mask times 1/scale must keep fp32 accuracy):
+    -1e4 on some keys (masking them), +-30 on others (they dominate their
+    rows), +-1e-3 on the rest; non-causal, d128.  (A row dominated by a
+    +1e4 key would have an LSE near 1e4, where fp32 spacing alone is about
+    1e-3, the LSE bound.)"""
+    p = workloads.make_prefill(134, 1, 257, 257, 2, 2, 128, "bf16")
+    rng = np.random.default_rng(135)
+    m = rng.standard_normal((1, 2, 1, 257)) * 1e-3
+    u = rng.random(m.shape)
+    m[u < 0.3] = -1e4
+    mid = u > 0.9
+    m[mid] = np.sign(rng.standard_normal(int(mid.sum()))) * 30.0
+    _case(p, m, "key mask of -1e4, +-30 and +-1e-3")
+
+
+def test_key_mask_non_default_scale():
+    """A softmax scale whose inverse is a 16-bit value (so two of the three
+    parts of 1/scale are zero) and one that needs all three, with -inf keys."""
+    for scale in (0.25, 0.0917):
+        p = workloads.make_prefill(136, 1, 200, 200, 2, 2, 128, "bf16", causal=True, scale=scale)
+        m = np.zeros((1, 1, 1, 200))
+        m[0, 0, 0, 150:] = -np.inf
+        m[0, 0, 0, :20] = 1.5
+        _case(p, m, f"key mask, scale {scale}")
 
 
 def test_mask_that_removes_whole_rows():

@@ -149,6 +149,10 @@ template <> struct E16<false> {
     static __device__ __forceinline__ float one(unsigned short b) {
         return __builtin_bit_cast(float, (unsigned)b << 16);
     }
+    // the largest bf16 value at or below x >= 0 (the upper 16 bits)
+    static __device__ __forceinline__ t down(float x) {
+        return __builtin_bit_cast(t, (unsigned short)(__builtin_bit_cast(unsigned, x) >> 16));
+    }
 };
 template <> struct E16<true> {
     using t = _Float16;
@@ -172,6 +176,13 @@ template <> struct E16<true> {
     }
     static __device__ __forceinline__ float one(unsigned short b) {
         return (float)__builtin_bit_cast(_Float16, b);
+    }
+    // the largest half value at or below x >= 0 (nearest, stepped down one
+    // unit when it rounded up; half bit patterns of x >= 0 are ordered)
+    static __device__ __forceinline__ t down(float x) {
+        const _Float16 h = (_Float16)x;
+        return (float)h > x ? __builtin_bit_cast(_Float16, (unsigned short)(__builtin_bit_cast(unsigned short, h) - 1))
+                            : h;
     }
 };
 
@@ -237,16 +248,19 @@ __device__ __forceinline__ void lds_dma16_s(const char *base, unsigned off, char
 
 // D: head_dim; ALIBI: add the per-head linear bias -m |pos - j| to the scores;
 // ROPE: rotate the query rows (RoPE) as they are loaded (keys arrive rotated);
-// MASK: add an explicit additive mask read from memory; F16: the inputs are
+// MASK: add an explicit additive mask read from memory (1: any mask, added in
+// the softmax step; 2: a key mask, the same row for every query, added by the
+// matrix cores as one more k-step of the S product); F16: the inputs are
 // IEEE half instead of bf16; PACK: a.gqa_pack query heads share the
 // workgroup (without it one head, and the work-item arithmetic is constant);
 // PERSIST (with PACK, no biases): one workgroup per CU walks the work items
 // (see below) instead of one workgroup per item.
-template <int D, bool ALIBI, bool ROPE, bool MASK, bool F16, bool PACK, bool PERSIST>
+template <int D, bool ALIBI, bool ROPE, int MASK, bool F16, bool PACK, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(PrefillArgs a) {
-    static_assert(!PERSIST || (PACK && !ALIBI && !ROPE && !MASK && D == 128), "persistent form: packed, no biases");
+    static_assert(!PERSIST || (PACK && !ALIBI && !ROPE && MASK == 0 && D == 128), "persistent form: packed, no biases");
+    static_assert(MASK >= 0 && MASK <= 2, "mask kind");
     using T = Tile<D>;
     using E = E16<F16>;
     using v8 = typename E::v8;
@@ -531,10 +545,36 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // score units (mask / scale)
     const unsigned short *mrow = nullptr;
     float inv_scale = 0.f;
-    if constexpr (MASK) {
+    if constexpr (MASK == 1) {
         mrow = (const unsigned short *)a.mask + b * a.m_sb + h * a.m_sh +
                (int64_t)min(qi, a.seqlen_q - 1) * a.m_ss;
         inv_scale = 1.f / a.scale;
+    }
+    // Key mask (MASK == 2): S^T[key][query] gains mask[key] / scale through
+    // one more k-step of the S product: the key operand holds the key's mask
+    // value m in dims 0-2, the query operand holds 1/scale split into three
+    // 16-bit parts (hi and mid rounded down, so that every part is >= 0 and
+    // an infinite m never meets parts of both signs; lo rounded to nearest),
+    // so the matrix core adds m hi + m mid + m lo: products of 16-bit values
+    // are exact in fp32 and the three parts hold all 24 bits of 1/scale, so
+    // this is m / scale to fp32 accuracy.  A dim whose part is zero carries 0,
+    // not m (an infinite m would give inf * 0).  Lanes of the upper half
+    // (dims 8-15) carry zeros.
+    v8 qmask = {};
+    unsigned kmask_nz = 0;                 // bit 0: mid part nonzero, bit 1: lo part nonzero
+    if constexpr (MASK == 2) {
+        mrow = (const unsigned short *)a.mask + b * a.m_sb + h * a.m_sh;
+        const float inv = 1.f / a.scale;   // > 0 (checked on the host)
+        const et ph = E::down(inv);
+        const float r1 = inv - (float)ph;
+        const et pm = E::down(r1);
+        const et pl = (et)(r1 - (float)pm);
+        if (half == 0) {
+            qmask[0] = ph;
+            qmask[1] = pm;
+            qmask[2] = pl;
+        }
+        kmask_nz = ((float)pm != 0.f ? 1u : 0u) | ((float)pl != 0.f ? 2u : 0u);
     }
 
     // matrix step of tile j: PV of tile j-1 (from vb), then S of tile j (from kb).
@@ -548,7 +588,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // beyond seqlen_k are never read.
     u32x4 mpre[2][2];
     auto prefetch_mask = [&](int j) __attribute__((always_inline)) {
-        if constexpr (MASK) {
+        if constexpr (MASK == 1) {
             const int k0 = (t_begin + tile_of(j)) * BN;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
@@ -566,6 +606,21 @@ void prefill_bf16_kernel(PrefillArgs a) {
                         mpre[sb][c] = w;
                     }
                 }
+        }
+    };
+    // Key mask of tile j (MASK == 2): the value of the lane's key row
+    // perm32(l32) of each 32-key sub-block, loaded at the end of the
+    // wavefront's matrix step of tile j - 1 (before the loop for its first
+    // tile); keys at or beyond seqlen_k read nothing and hold 0.
+    unsigned kmv[2] = {0u, 0u};
+    auto prefetch_kmask = [&](int j) __attribute__((always_inline)) {
+        if constexpr (MASK == 2) {
+            const int k0 = (t_begin + tile_of(j)) * BN;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int key = k0 + sb * 32 + kr;
+                kmv[sb] = key < a.seqlen_k ? (unsigned)mrow[key] : 0u;
+            }
         }
     };
     auto matrix_step = [&](int j, const char *kb, const char *vb) {
@@ -610,19 +665,31 @@ void prefill_bf16_kernel(PrefillArgs a) {
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+            if constexpr (MASK == 2) {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const unsigned m = half == 0 ? kmv[sb] : 0u;
+                    const unsigned w0 = m | ((kmask_nz & 1u) ? m << 16 : 0u);
+                    const unsigned w1 = (kmask_nz & 2u) ? m : 0u;
+                    s[sb] = E::mfma(__builtin_bit_cast(v8, u32x4{w0, w1, 0u, 0u}), qmask, s[sb]);
+                }
+            }
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
                     s[sb] = E::mfma(kf[ks][sb], qf[ks], s[sb]);
-            // 1 DS read per MFMA, kept 4 MFMAs ahead
+            // 1 DS read per MFMA, kept 4 MFMAs ahead (the key-mask products
+            // need no read and go first)
             __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+            if constexpr (MASK == 2) __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
 #pragma unroll
             for (int i = 0; i < 2 * KSTEPS - 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+            if (j + 1 < w_hi) prefetch_kmask(j + 1);
         }
     };
 
@@ -645,7 +712,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
                     s[sb][r] = __builtin_fmaf(dist, alibi_raw, s[sb][r]);
                 }
         }
-        if constexpr (MASK) {
+        if constexpr (MASK == 1) {
             // the lane's keys are four runs of 8: k0 + 32 sb + 16 c + 8 half + e
             // (prefetched in the matrix step; keys past seqlen_k hold 0)
 #pragma unroll
@@ -724,6 +791,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // LDS buffer is named statically.
     const int nph = ntiles > 0 ? 2 * ntiles + 2 : 0;
     if (ntiles > 0) issue_k(0, sK0);
+    if (w_lo < w_hi) prefetch_kmask(w_lo);
     rope_tables();
     if (grp == 0) rotate_q();
     wait_loads();
@@ -823,15 +891,19 @@ void launch_mask(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t s) {
     // per workgroup (valid for any group)
     constexpr bool CAN_PACK = D == 128 && !F16;
     constexpr bool CAN_PERSIST = CAN_PACK && !ALIBI && !ROPE;
+    // a mask whose rows do not depend on the query (row stride 0) is a key mask
+    const int mk = !a.mask ? 0 : (a.m_ss == 0 ? 2 : 1);
     if (a.gqa_pack > 1 && CAN_PERSIST && !a.mask && a.persist_wgs > 0 && grid.x > (unsigned)a.persist_wgs) {
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, F16, CAN_PACK, CAN_PERSIST>),
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, 0, F16, CAN_PACK, CAN_PERSIST>),
                            dim3(a.persist_wgs), block, 0, s, a);
     } else if (a.gqa_pack > 1 && CAN_PACK) {
-        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, CAN_PACK, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, CAN_PACK, false>), grid, block, 0, s, a);
+        if (mk == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, 2, F16, CAN_PACK, false>), grid, block, 0, s, a);
+        else if (mk == 1) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, 1, F16, CAN_PACK, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, 0, F16, CAN_PACK, false>), grid, block, 0, s, a);
     } else {
-        if (a.mask) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, true, F16, false, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, false, F16, false, false>), grid, block, 0, s, a);
+        if (mk == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, 2, F16, false, false>), grid, block, 0, s, a);
+        else if (mk == 1) hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, 1, F16, false, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<D, ALIBI, ROPE, 0, F16, false, false>), grid, block, 0, s, a);
     }
 }
 
