@@ -139,7 +139,9 @@ typedef enum {
  * mask_stride[0..2] multiples of 8 elements (bf16, f16) or 4 (fp32).  Values
  * are read on the device and not validated.  The implicit masks stay the
  * cheap way to express causal, window and padding: an explicit mask adds
- * its bytes to every query tile's traffic.
+ * its bytes to every query tile's traffic.  A 16-bit mask with
+ * mask_stride[2] == 0 (the same row for every query) is added by the matrix
+ * cores and costs less than one whose rows differ.
  *
  * Requirements: head_dim in {64, 128}; heads_q % heads_kv == 0;
  * softmax_scale finite and > 0 (the usual value is 1/sqrt(head_dim));
