@@ -40,13 +40,13 @@
 //
 // Matrix/vector overlap (the page's Cube/Vector pipelining, jsqmd.com
 // section 二, done the gfx950 way): the 8 wavefronts form two groups of 4,
-// one wavefront of each group per SIMD.  Time is cut into phases separated
-// by workgroup barriers; in every phase one group runs its matrix step
-// (PV of the previous tile, then S = K Q^T of the current tile: 32 MFMAs)
-// while the other group runs its softmax step on the VALU (max, exp, P in
-// bf16, row sums, rare O rescale).  Group B lags group A by one phase, so
-// each SIMD always has one wavefront feeding the matrix core and one feeding
-// the vector ALU.
+// one wavefront of each group per SIMD.  Time is cut into phases, two per
+// tile, with a workgroup barrier after every second one; in every phase one
+// group runs its matrix step (PV of the previous tile, then S = K Q^T of the
+// current tile: 32 MFMAs) while the other group runs its softmax step on the
+// VALU (max, exp, P in bf16, row sums, rare O rescale).  Group B lags group
+// A by one phase, so each SIMD has one wavefront feeding the matrix core and
+// one feeding the vector ALU.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, 64 lanes):
 //   S^T[key][query] = K Q^T : A = K rows from LDS, B = Q held in registers.
@@ -788,7 +788,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // step 2j is the matrix step of tile j, step 2j+1 its softmax step.  At
     // even phase 2j every wavefront issues K of tile j+1 and V of tile j; they
     // must land by the end of phase 2j+1.  Unrolled by four phases so every
-    // LDS buffer is named statically.
+    // LDS buffer is named statically.  Only the odd phases end in a barrier:
+    // the loads of phase 2j go into the buffers that tile j-1 used, whose
+    // last reader (the lagging group's matrix step of tile j-1) ends in phase
+    // 2j-1, and tile j+1's buffers are next read in phase 2j+2, after the
+    // barrier that follows their wait.  A barrier after the even phases as
+    // well, which only kept the two groups in lockstep, measured slightly
+    // slower.
     const int nph = ntiles > 0 ? 2 * ntiles + 2 : 0;
     if (ntiles > 0) issue_k(0, sK0);
     if (w_lo < w_hi) prefetch_kmask(w_lo);
@@ -804,7 +810,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if (j < ntiles) issue_v(j, sV0);
         if (grp == 0) matrix_step(j, sK0, sV1);
         else softmax_step(j - 1);
-        phase_barrier();
         // phase p+1: leading: softmax(j) ; lagging: matrix(j)
         if (grp == 0) softmax_step(j);
         else matrix_step(j, sK0, sV1);
@@ -816,7 +821,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if (j + 1 < ntiles) issue_v(j + 1, sV1);
         if (grp == 0) matrix_step(j + 1, sK1, sV0);
         else softmax_step(j);
-        phase_barrier();
         // phase p+3: leading: softmax(j+1) ; lagging: matrix(j+1)
         if (grp == 0) softmax_step(j + 1);
         else matrix_step(j + 1, sK1, sV0);
