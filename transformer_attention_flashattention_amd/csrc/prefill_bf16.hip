@@ -217,24 +217,30 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // One direct-to-LDS load: each lane moves 16 bytes from its global address g
-// to LDS address l0 + 16 * lane, l0 being the wavefront-uniform LDS address l
-// of lane 0 (passed in M0, which needs one wait state before the load reads
-// it).  Issued as inline assembly so that the compiler's wait-count pass does
-// not see an in-flight load that also writes LDS: it would then drain every
-// LDS read of the loop to zero (lgkmcnt(0)) while the load is outstanding.
-// Completion is tracked explicitly with wait_loads() and the barrier after it.
-__device__ __forceinline__ void lds_dma16(const char *g, char *l) {
-    const unsigned la = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)l;
+// to LDS address la + 16 * lane, la being the wavefront-uniform 32-bit LDS
+// address of lane 0 (passed in M0, which needs one wait state before the load
+// reads it).  Issued as inline assembly so that the compiler's wait-count pass
+// does not see an in-flight load that also writes LDS: it would then drain
+// every LDS read of the loop to zero (lgkmcnt(0)) while the load is
+// outstanding.  Completion is tracked explicitly with wait_loads() and the
+// barrier after it.  The LDS address travels as a 32-bit LDS offset: from a
+// generic pointer the compiler would read it back with two readfirstlanes and
+// a null check per load, on the critical softmax step of the lagging group.
+__device__ __forceinline__ void lds_dma16(const char *g, unsigned la) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(g), "s"(__builtin_amdgcn_readfirstlane(la))
                  : "memory", "m0");
 }
 
+// 32-bit LDS address of a location in a __shared__ array
+__device__ __forceinline__ unsigned lds_addr(const char *l) {
+    return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char *)l;
+}
+
 // The same load with a wavefront-uniform base address (in SGPRs) and a 32-bit
 // per-lane offset, which holds one VGPR per load instead of two.
-__device__ __forceinline__ void lds_dma16_s(const char *base, unsigned off, char *l) {
-    const unsigned la = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)l;
+__device__ __forceinline__ void lds_dma16_s(const char *base, unsigned off, unsigned la) {
     // the base is the same in every lane; readfirstlane makes that visible,
     // so that it lives in SGPRs as the instruction's base operand requires
     const uint64_t bu = (uint64_t)(uintptr_t)base;
@@ -320,6 +326,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
         char *buf = (wave >> 1) == 0 ? sK0 : (wave >> 1) == 1 ? sK1 : (wave >> 1) == 2 ? sV0 : sV1;
         return buf + (wave & 1) * 8192;
     };
+    // the tile buffers' LDS addresses, and this wavefront's index as a
+    // uniform value (its share of a tile)
+    const unsigned lK0 = lds_addr(sK0), lK1 = lds_addr(sK1), lV0 = lds_addr(sV0), lV1 = lds_addr(sV1);
+    const unsigned wave_u = (unsigned)__builtin_amdgcn_readfirstlane(wave);
     bool have_next = false;
     for (int round = 0;; ++round) {
     const unsigned wi = PERSIST ? (unsigned)item_of(round) : blockIdx.x;
@@ -476,14 +486,17 @@ void prefill_bf16_kernel(PrefillArgs a) {
         k_loff[i] = (unsigned)(r * k_row_bytes) + (unsigned)(T::k_chunk(r, p) << 4);
         v_loff[i] = (unsigned)(r * v_row_bytes) + (unsigned)(T::v_chunk(r, p) << 4);
     }
-    auto issue = [&](const char *base, int64_t row_bytes, const unsigned *loff, int t, char *buf,
+    // (lbuf: the tile buffer's LDS address; full tiles take a uniform base
+    // in SGPRs plus the lane's 32-bit offset)
+    auto issue = [&](const char *base, int64_t row_bytes, const unsigned *loff, int t, unsigned lbuf,
                      bool is_k) {
         const int k0 = (t_begin + tile_of(t)) * BN;
         const char *tb = base + (int64_t)k0 * row_bytes;
+        const unsigned lb = lbuf + wave_u * (T::LOADS_PER_WAVE * 1024);
         if (k0 + BN <= Lk) {
 #pragma unroll
             for (int i = 0; i < T::LOADS_PER_WAVE; ++i)
-                lds_dma16(tb + loff[i], buf + (wave * T::LOADS_PER_WAVE + i) * 1024);
+                lds_dma16_s(tb, loff[i], lb + i * 1024);
         } else {
             // last tile: rows past the valid length re-read the last valid row
 #pragma unroll
@@ -493,13 +506,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 const int p = (lin % T::ROWB) >> 4;
                 const int row = min(k0 + r, Lk - 1);
                 const int c = is_k ? T::k_chunk(r, p) : T::v_chunk(r, p);
-                lds_dma16(base + (int64_t)row * row_bytes + (c << 4),
-                          buf + (wave * T::LOADS_PER_WAVE + i) * 1024);
+                lds_dma16(base + (int64_t)row * row_bytes + (c << 4), lb + i * 1024);
             }
         }
     };
-    auto issue_k = [&](int t, char *buf) { issue(Kp, k_row_bytes, k_loff, t, buf, true); };
-    auto issue_v = [&](int t, char *buf) { issue(Vp, v_row_bytes, v_loff, t, buf, false); };
+    auto issue_k = [&](int t, unsigned lbuf) { issue(Kp, k_row_bytes, k_loff, t, lbuf, true); };
+    auto issue_v = [&](int t, unsigned lbuf) { issue(Vp, v_row_bytes, v_loff, t, lbuf, false); };
 
     // ---- per-lane LDS operand offsets (loop invariant) ----------------------
     const int kr = perm32(l32);                      // K row within a 32-key sub-block
@@ -796,7 +808,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // well, which only kept the two groups in lockstep, measured slightly
     // slower.
     const int nph = ntiles > 0 ? 2 * ntiles + 2 : 0;
-    if (ntiles > 0) issue_k(0, sK0);
+    if (ntiles > 0) issue_k(0, lK0);
     if (w_lo < w_hi) prefetch_kmask(w_lo);
     rope_tables();
     if (grp == 0) rotate_q();
@@ -806,8 +818,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
     for (int p = 0; p < nph; p += 4) {
         const int j = p >> 1;             // even tile index of this unrolled block
         // phase p (= 2j): leading: matrix(j) ; lagging: softmax(j-1)
-        if (j + 1 < ntiles) issue_k(j + 1, sK1);
-        if (j < ntiles) issue_v(j, sV0);
+        if (j + 1 < ntiles) issue_k(j + 1, lK1);
+        if (j < ntiles) issue_v(j, lV0);
         if (grp == 0) matrix_step(j, sK0, sV1);
         else softmax_step(j - 1);
         // phase p+1: leading: softmax(j) ; lagging: matrix(j)
@@ -817,8 +829,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
         phase_barrier();
         if (p + 2 >= nph) break;
         // phase p+2 (= 2(j+1)): leading: matrix(j+1) ; lagging: softmax(j)
-        if (j + 2 < ntiles) issue_k(j + 2, sK0);
-        if (j + 1 < ntiles) issue_v(j + 1, sV1);
+        if (j + 2 < ntiles) issue_k(j + 2, lK0);
+        if (j + 1 < ntiles) issue_v(j + 1, lV1);
         if (grp == 0) matrix_step(j + 1, sK1, sV0);
         else softmax_step(j);
         // phase p+3: leading: softmax(j+1) ; lagging: matrix(j+1)
@@ -858,7 +870,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 const int r = i * 4 + (ln >> 4);              // row of the 32 this lane's chunk is in
                 const int c = (ln & 15) ^ (r & 15);           // the chunk that belongs at this slot
                 const int row = max(0, min(q0w2 + r, Lq2 - 1));
-                lds_dma16_s(qb, (unsigned)((row - rb) * a.q_ss * 2) + (c << 4), stage + i * 1024);
+                lds_dma16_s(qb, (unsigned)((row - rb) * a.q_ss * 2) + (c << 4), lds_addr(stage + i * 1024));
             }
         }
     }
