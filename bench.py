@@ -43,6 +43,7 @@ import argparse
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -123,6 +124,8 @@ def parse():
                     help="heads of the causal N=8192 workload the CPU oracle times")
     ap.add_argument("--decode-chunk", type=int, default=0,
                     help="keys per decode split (0 = library choice)")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="do not read the shader clock with amd-smi during the run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -269,6 +272,84 @@ def roofline(bound, achieved, peak, unit, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+def start_clock_sampler(seconds):
+    """Start a child process group that reads the shader clocks (one value per
+    XCD) with a single amd-smi call about every second.  Started before this
+    process makes its first GPU call; skipped under a profiler (its injected
+    library would follow the child) or when amd-smi is missing.  Returns a
+    handle or None."""
+    import shutil
+    import subprocess
+    import tempfile
+    if any(k.startswith(("ROCPROF", "ROCP_")) for k in os.environ) or \
+            "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe) or not shutil.which("bash"):
+        return None
+    out = tempfile.NamedTemporaryFile(prefix="fa_bench_sclk_", suffix=".json", delete=False)
+    loop = (f"for i in $(seq {int(seconds)}); do echo \"@T $(date +%s.%N)\"; "
+            f"'{exe}' metric -g 0 --clock --json; sleep 0.5; done")
+    try:
+        proc = subprocess.Popen(["bash", "-c", loop], stdout=out, stderr=subprocess.DEVNULL,
+                                stdin=subprocess.DEVNULL, start_new_session=True)
+    except OSError:
+        out.close()
+        os.unlink(out.name)
+        return None
+    return proc, out
+
+
+def finish_clock_sampler(handle, windows=None):
+    """Stop the sampler and summarise the shader clocks it read while the GPU
+    was busy (samples of 1000 MHz or more; an idle GPU reads about 100), over
+    the whole run and inside each named (start, end) time window."""
+    import signal
+    if handle is None:
+        return None
+    proc, out = handle
+    if proc.poll() is None:
+        try:
+            os.killpg(proc.pid, signal.SIGTERM)      # the loop and its current amd-smi call
+        except OSError:
+            pass
+    try:
+        proc.wait(timeout=10)
+    except Exception:
+        proc.kill()
+        proc.wait()
+    out.close()
+    try:
+        with open(out.name) as f:
+            text = f.read()
+    finally:
+        os.unlink(out.name)
+    # each amd-smi call follows a "@T <unix time>" line written just before it
+    samples = []                                    # (time, MHz)
+    for part in re.split(r"^@T ", text, flags=re.M)[1:]:
+        head, _, body = part.partition("\n")
+        try:
+            t = float(head.strip())
+        except ValueError:
+            continue
+        for v in re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)', body):
+            samples.append((t, int(v)))
+
+    def stats(vals):
+        busy = sorted(v for v in vals if v >= 1000)
+        d = {"samples": len(vals), "busy_samples": len(busy)}
+        if busy:
+            d.update({"busy_median_mhz": busy[len(busy) // 2], "busy_min_mhz": busy[0],
+                      "busy_max_mhz": busy[-1]})
+        return d
+
+    summary = {"tool": "amd-smi metric --clock about twice a second, every XCD"}
+    summary.update(stats([v for _, v in samples]))
+    for name, (t0, t1) in (windows or {}).items():
+        summary[name] = stats([v for t, v in samples if t0 <= t <= t1])
+    return summary
+
+
 def ms_stats(ms):
     return {"ms_mean": round(float(ms.mean()), 4), "ms_median": round(float(np.median(ms)), 4),
             "ms_min": round(float(ms.min()), 4), "calls": int(len(ms))}
@@ -284,6 +365,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+
+    sampler = None if (args.copy_calibration or args.no_clock_sample) else start_clock_sampler(900)
 
     import torch
     import transformer_attention_flashattention_amd as fa
@@ -575,6 +658,19 @@ def main():
         "roofline_decode": configs["config5"]["roofline"],
         "host": platform.node(),
     }
+    # shader clock over the GPU part of the run, and inside a window of about
+    # 4 s of back-to-back calls of the causal N = 8192 prefill (none under a
+    # profiler)
+    windows = {}
+    if sampler is not None:
+        n_calls = max(1, int(4000.0 / max(float(pre_ms.mean()), 1e-3)))
+        t_start = time.time()
+        for _ in range(n_calls):
+            fa.prefill(q, k, v, causal=True, scale=p.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        # an amd-smi call reads the clock a few tenths of a second after its timestamp
+        windows["prefill_window"] = (t_start + 0.2, time.time() - 1.0)
+    result["sclk"] = finish_clock_sampler(sampler, windows)
 
     if not args.no_cpu_baseline:
         info = host_info()
