@@ -3,14 +3,15 @@
 // full fp32 precision (no 16-bit rounding of Q, K or P anywhere), which the
 // fp32 tolerance of the method needs.
 //
-// One workgroup = 4 wavefronts = 16 query rows of one (batch, head).  Four
+// One workgroup = 8 wavefronts = 16 query rows of one (batch, head).  Four
 // consecutive lanes share a query row, each holding a quarter of its dims
 // (16-byte chunks c = sub, sub + 4, ...), so a score is four partial dot
 // products summed across the quad.  The wavefronts split the row block's
-// visible key tiles (16 keys each; wavefront w takes tiles w, w + 4, ...),
+// visible key tiles (16 keys each; wavefront w takes tiles w, w + 8, ...;
+// two wavefronts per SIMD hide each other's LDS and memory latency),
 // each keeping its own running max and sum per row (hwcomputing.csdn.net
 // page, section 2.2), and merge their partial results through LDS once at
-// the end: the serial work of a lane is a sixteenth of one lane per row over
+// the end: the serial work of a lane is a thirty-second of one lane per row over
 // all keys.  Each wavefront stages its tiles in LDS private to it, so the
 // tile loop needs no workgroup barrier.  Tiles outside the causal / window /
 // valid-length band are skipped and padding rows are zero-filled, never
@@ -24,7 +25,7 @@ namespace fa {
 namespace {
 
 constexpr int BM = kPrefillF32BM;   // query rows per workgroup
-constexpr int NW = 4;               // wavefronts per workgroup
+constexpr int NW = 8;               // wavefronts per workgroup
 constexpr int BN = 16;              // keys per tile
 constexpr float LN2 = 0.693147180559945309f;
 
