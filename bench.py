@@ -288,8 +288,9 @@ def start_clock_sampler(seconds):
     if not os.path.exists(exe) or not shutil.which("bash"):
         return None
     out = tempfile.NamedTemporaryFile(prefix="fa_bench_sclk_", suffix=".json", delete=False)
-    loop = (f"for i in $(seq {int(seconds)}); do echo \"@T $(date +%s.%N)\"; "
-            f"'{exe}' metric -g 0 --clock --json; sleep 0.5; done")
+    # the loop ends on its own once this process is gone or after `seconds`
+    loop = (f"while kill -0 {os.getpid()} 2>/dev/null && [ $SECONDS -lt {int(seconds)} ]; do "
+            f"echo \"@T $(date +%s.%N)\"; '{exe}' metric -g 0 --clock --json; sleep 0.5; done")
     try:
         proc = subprocess.Popen(["bash", "-c", loop], stdout=out, stderr=subprocess.DEVNULL,
                                 stdin=subprocess.DEVNULL, start_new_session=True)
@@ -297,22 +298,28 @@ def start_clock_sampler(seconds):
         out.close()
         os.unlink(out.name)
         return None
+    import atexit
+    atexit.register(_stop_group, proc)
     return proc, out
+
+
+def _stop_group(proc):
+    import signal
+    if proc.poll() is None:
+        try:
+            os.killpg(proc.pid, signal.SIGTERM)      # the loop and its current amd-smi call
+        except OSError:
+            pass
 
 
 def finish_clock_sampler(handle, windows=None):
     """Stop the sampler and summarise the shader clocks it read while the GPU
     was busy (samples of 1000 MHz or more; an idle GPU reads about 100), over
     the whole run and inside each named (start, end) time window."""
-    import signal
     if handle is None:
         return None
     proc, out = handle
-    if proc.poll() is None:
-        try:
-            os.killpg(proc.pid, signal.SIGTERM)      # the loop and its current amd-smi call
-        except OSError:
-            pass
+    _stop_group(proc)
     try:
         proc.wait(timeout=10)
     except Exception:
