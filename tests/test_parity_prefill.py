@@ -85,6 +85,17 @@ def test_ragged_lengths(N, causal):
           f"ragged N{N} causal={causal}")
 
 
+@pytest.mark.parametrize("N", [1, 2, 15, 16, 17, 127, 129, 143])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_ragged_lengths(N, causal, d):
+    """The fp32 kernel's eight wavefronts take alternate 16-key tiles: below
+    eight tiles some wavefronts merge an empty partial (max -inf, sum 0), and
+    the last tile is ragged.  MQA (one KV head)."""
+    _case(workloads.make_prefill(300 + N + d, 2, N, N, 2, 1, d, "f32", causal=causal),
+          f"fp32 ragged N{N} d{d} causal={causal}")
+
+
 @pytest.mark.parametrize("W", [1, 63, 64, 65, 200, 700])
 def test_causal_windows(W):
     _case(workloads.make_prefill(200 + W, 1, 600, 600, 4, 2, 128, "bf16", causal=True,
